@@ -1,0 +1,274 @@
+/*
+ * pagedkv.h — C ABI of the paged KV-cache attention library for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * What the library computes (reference pages, by title and section):
+ *   - Paged KV cache: keys and values in fixed-size pages of one shared pool,
+ *     allocated on demand; a per-sequence block table maps logical page i to a
+ *     physical page, so storage is non-contiguous; repeated prompt prefixes may
+ *     share pages.  "TensorRT-LLM框架解析与高性能推理优化实践" §4.2 (KV缓存管理细节:
+ *     KVCacheBlock / KVCacheManager with allocate_blocks, free_blocks,
+ *     get_block_table) and §6.2 (Paged Attention优化).
+ *   - Attention: scaled dot-product softmax attention ("TensorRT-LLM性能调优：提升LLM
+ *     推理效率", layer-fusion discussion: fused MHA with scaled dot-product
+ *     attention and a causal mask), computed flash-style with a running max
+ *     and running sum (first page, §6.1 Flash Attention实现).
+ *   - KV-cache quantization with one scale per attention head, dequantised
+ *     inside the attention kernel (first page, §7.2 KV Cache量化).
+ *   - Chunked context: long prompts processed chunk by chunk, interleaved with
+ *     decode requests (first page, §5.3 分块上下文处理); in-flight batching of
+ *     mixed-length requests ("TensorRT-LLM内核融合与动态批处理", In-flight Batching
+ *     section).
+ *   - Launches are asynchronous and stream-ordered (first page, §2.2 GPU内存传输机制).
+ *
+ * Conventions for every call below:
+ *   - Pointers named as device pointers are HIP device memory owned by the
+ *     caller.  The library allocates no device memory and keeps no device state
+ *     between calls; scratch space is passed in as `workspace`.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Launch
+ *     calls enqueue work and return without synchronizing.
+ *   - Host-side checks happen before anything is launched: on a non-OK status
+ *     nothing was enqueued and pkv_last_error() (thread-local) says why.
+ *   - Device-resident values (block-table entries, lengths, offsets) are trusted
+ *     on the fast path: they must satisfy the documented ranges.  An entry
+ *     point that reads them only on the device cannot check them;
+ *     pkv_validate_block_tables() checks them (synchronously) for debugging.
+ *
+ * Layouts (row-major, element type given by the dtype):
+ *   K pool, V pool : [num_pages][num_kv_heads][page_size][head_dim]
+ *                    token t of a sequence with block-table row `bt` lives in
+ *                    page bt[t / page_size], slot t % page_size.
+ *   block tables   : int32 [rows][bt_stride]; unused entries may hold -1.
+ *   decode q/out   : [num_seqs][num_q_heads][head_dim]
+ *   packed tokens  : [num_tokens][heads][head_dim], rows laid end to end
+ *                    (no padding), described by int32 offsets cu[rows+1].
+ *   lse            : float [rows][num_q_heads], natural-log log-sum-exp of the
+ *                    scaled scores (-inf for an empty context).
+ *   Query head h reads KV head h / (num_q_heads / num_kv_heads).
+ */
+#ifndef PAGEDKV_H_
+#define PAGEDKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pkv_status {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = 1,     /* null pointer, negative size, bad combination */
+  PKV_ERR_UNSUPPORTED = 2,     /* valid but not implemented (dtype, head_dim, page size) */
+  PKV_ERR_OUT_OF_PAGES = 3,    /* allocator: not enough free pages (nothing taken) */
+  PKV_ERR_BAD_BLOCK_TABLE = 4, /* validate: an entry outside the pool or a length too long */
+  PKV_ERR_HIP = 5              /* a HIP runtime call failed; message has the HIP error */
+} pkv_status;
+
+typedef enum pkv_dtype {
+  PKV_F32 = 0,
+  PKV_BF16 = 1,
+  PKV_FP8_E4M3FN = 2           /* OCP e4m3fn: bias 7, max 448, no inf, NaN = 0x7F/0xFF */
+} pkv_dtype;
+
+/* One layer's paged cache.  Supported: kv_dtype F32, BF16 or FP8_E4M3FN;
+ * head_dim 64 or 128; page_size 16, 32 or 64; num_kv_heads >= 1.
+ * k_scale / v_scale: device float[num_kv_heads], required iff kv_dtype is
+ * FP8_E4M3FN (stored value = x / scale, dequantised value = code * scale). */
+typedef struct pkv_cache_desc {
+  void* k_pool;
+  void* v_pool;
+  const float* k_scale;
+  const float* v_scale;
+  int32_t num_pages;
+  int32_t num_kv_heads;
+  int32_t page_size;
+  int32_t head_dim;
+  int32_t kv_dtype;            /* a pkv_dtype */
+} pkv_cache_desc;
+
+/* Library version string (static storage). */
+const char* pkv_version(void);
+
+/* Message for the last non-OK status returned on this thread (static,
+ * thread-local storage; overwritten by the next failing call). */
+const char* pkv_last_error(void);
+
+/* ------------------------------------------------------------------------ *
+ * Host page allocator — "TensorRT-LLM框架解析与高性能推理优化实践" §4.2 (KVCacheManager:
+ * allocate_blocks / free_blocks; block reuse and prefix sharing) and §5.2
+ * (OutOfMemoryError when no pages remain).  CPU only; every call is
+ * serialised by an internal mutex.  Page ids are 0..num_pages-1.  A page's
+ * refcount is 1 after allocation, +1 per share, -1 per free; it returns to the
+ * free list at 0.  Which free ids an allocation receives is unspecified.
+ * ------------------------------------------------------------------------ */
+
+/* Create an allocator for `num_pages` (> 0) pages; *out_alloc receives the handle. */
+pkv_status pkv_allocator_create(int32_t num_pages, void** out_alloc);
+
+/* Destroy an allocator (NULL is ignored). */
+void pkv_allocator_destroy(void* alloc);
+
+/* Allocate `n` (>= 0) pages into host array out_ids[n].  All or nothing:
+ * PKV_ERR_OUT_OF_PAGES leaves the allocator unchanged. */
+pkv_status pkv_alloc_pages(void* alloc, int32_t n, int32_t* out_ids);
+
+/* Add one reference to each of the n allocated pages ids[n] (shared prefix).
+ * PKV_ERR_INVALID_ARG (and no change) if an id is out of range or free. */
+pkv_status pkv_share_pages(void* alloc, int32_t n, const int32_t* ids);
+
+/* Drop one reference from each of ids[n]; pages reaching 0 become free.
+ * PKV_ERR_INVALID_ARG (and no change) if an id is out of range, free, or
+ * would be released more times than it is referenced. */
+pkv_status pkv_free_pages(void* alloc, int32_t n, const int32_t* ids);
+
+/* Number of free pages, or -1 for a NULL handle. */
+int32_t pkv_num_free_pages(const void* alloc);
+
+/* Reference count of page `id` (0 = free), or -1 if the handle or id is invalid. */
+int32_t pkv_page_refcount(const void* alloc, int32_t id);
+
+/* ------------------------------------------------------------------------ *
+ * kv_cache_append — scatter new tokens' K and V into their page slots
+ * ("TensorRT-LLM内核融合与动态批处理", In-flight Batching section: a request's KV
+ * is placed as it joins and grows; first page §7.2 for the fp8 path).
+ *
+ * k_new, v_new : device [num_new_tokens][num_kv_heads][head_dim], packed rows.
+ *                in_dtype must equal the cache dtype for F32/BF16 caches (a copy);
+ *                an FP8 cache takes F32 input and stores
+ *                e4m3fn(x / scale[head]): IEEE float32 division, round to
+ *                nearest even, saturating to +-448; NaN stays NaN.
+ * cu_new_tokens: device int32[num_rows+1], cu[0] = 0, non-decreasing,
+ *                cu[num_rows] = num_new_tokens.
+ * start_pos    : device int32[num_rows]; row r's token i goes to logical
+ *                position start_pos[r] + i of block-table row r.
+ * block_tables : device int32[num_rows][bt_stride]; every page the new tokens
+ *                land in must be a valid id.
+ * Pages written must not be shared with another row that reads them in the
+ * same stream step (shared prefixes are full pages, never appended to).
+ * Bytes of the pool other than the written slots are left unchanged.
+ * ------------------------------------------------------------------------ */
+pkv_status pkv_kv_cache_append(const pkv_cache_desc* cache,
+                               const void* k_new, const void* v_new, int32_t in_dtype,
+                               const int32_t* cu_new_tokens, const int32_t* start_pos,
+                               const int32_t* block_tables, int32_t bt_stride,
+                               int32_t num_rows, int32_t num_new_tokens, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * paged_attn_decode — one query token per sequence over its paged context
+ * ("TensorRT-LLM框架解析与高性能推理优化实践" §6.2: the kernel walks the sequence's
+ * block table; §6.1: running max / running sum).  Work is split along the
+ * context into ranges of `split_tokens` tokens (flash-decoding); each range
+ * leaves a partial (max, sum, unnormalised accumulator) in the workspace and
+ * a log-sum-exp merge combines them.  Sequences that fit in one range are
+ * written directly.
+ *
+ * Supported (q_dtype, kv_dtype, out_dtype): (F32, F32, F32), (BF16, BF16, BF16),
+ * (BF16, FP8_E4M3FN, BF16).  num_q_heads must be a multiple of num_kv_heads
+ * with group size G = num_q_heads / num_kv_heads <= 16.
+ *
+ * q            : device [num_seqs][num_q_heads][head_dim]
+ * out          : device [num_seqs][num_q_heads][head_dim]
+ * lse          : device float[num_seqs][num_q_heads] or NULL
+ * block_tables : device int32[num_seqs][bt_stride]
+ * context_lens : device int32[num_seqs], 0 <= L <= min(max_context_len,
+ *                bt_stride * page_size); L counts the query's own token.
+ *                L = 0 gives out = 0 and lse = -inf.
+ * sm_scale     : score scale (1/sqrt(head_dim) for standard attention).
+ * split_tokens : context range per work item, a positive multiple of
+ *                page_size; 0 selects pkv_decode_split_tokens().
+ * workspace    : device scratch of at least pkv_decode_workspace_bytes(...)
+ *                bytes (may be NULL when that size is 0); contents on entry
+ *                are ignored.
+ * ------------------------------------------------------------------------ */
+
+/* Default split length for a decode batch: a multiple of page_size chosen
+ * from the batch shape so that the launch has enough work items to fill the
+ * device.  Pure host function; returns 0 on invalid arguments. */
+int32_t pkv_decode_split_tokens(const pkv_cache_desc* cache, int32_t num_seqs,
+                                int32_t num_q_heads, int32_t max_context_len);
+
+/* Workspace bytes needed by a decode call with these arguments (split_tokens
+ * resolved as in pkv_paged_attn_decode; 0 when no sequence can need more than
+ * one range). */
+size_t pkv_decode_workspace_bytes(const pkv_cache_desc* cache, int32_t num_seqs,
+                                  int32_t num_q_heads, int32_t max_context_len,
+                                  int32_t split_tokens);
+
+/* Partial pass followed by the merge pass. */
+pkv_status pkv_paged_attn_decode(const pkv_cache_desc* cache,
+                                 const void* q, int32_t q_dtype,
+                                 void* out, int32_t out_dtype, float* lse,
+                                 const int32_t* block_tables, int32_t bt_stride,
+                                 const int32_t* context_lens, int32_t num_seqs,
+                                 int32_t num_q_heads, int32_t max_context_len,
+                                 float sm_scale, int32_t split_tokens,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* The partial pass alone: writes out/lse of single-range sequences and the
+ * workspace partials of the others.  pkv_lse_merge with the same arguments
+ * completes the call. */
+pkv_status pkv_paged_attn_decode_partial(const pkv_cache_desc* cache,
+                                         const void* q, int32_t q_dtype,
+                                         void* out, int32_t out_dtype, float* lse,
+                                         const int32_t* block_tables, int32_t bt_stride,
+                                         const int32_t* context_lens, int32_t num_seqs,
+                                         int32_t num_q_heads, int32_t max_context_len,
+                                         float sm_scale, int32_t split_tokens,
+                                         void* workspace, size_t workspace_bytes,
+                                         void* stream);
+
+/* The log-sum-exp merge pass: for every sequence with more than one range,
+ * M = max_s m_s, w_s = exp(m_s - M), out = sum_s w_s acc_s / sum_s w_s l_s,
+ * lse = M + ln(sum_s w_s l_s).  Sequences with one range are untouched. */
+pkv_status pkv_lse_merge(const pkv_cache_desc* cache, void* out, int32_t out_dtype, float* lse,
+                         const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                         int32_t max_context_len, int32_t split_tokens,
+                         const void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * paged_attn_chunked_prefill — causal attention of context chunks over the
+ * pages already cached for their request plus the chunk itself
+ * (first page §5.3 分块上下文处理; causal mask of the fused-MHA pseudocode in
+ * "TensorRT-LLM性能调优：提升LLM推理效率").  The chunk's own K/V must already be
+ * in the pages (pkv_kv_cache_append).  Row i of request r (absolute position
+ * ctx_before[r] + i) attends keys 0 .. ctx_before[r] + i inclusive.
+ *
+ * q, out     : device packed [num_q_tokens][num_q_heads][head_dim]
+ * lse        : device float[num_q_tokens][num_q_heads] or NULL
+ * cu_q_lens  : device int32[num_reqs+1], chunk row offsets, cu[0] = 0,
+ *              every chunk length <= max_chunk_len, cu[num_reqs] = num_q_tokens
+ * ctx_before : device int32[num_reqs], tokens cached before the chunk;
+ *              ctx_before[r] + chunk_len(r) <= bt_stride * page_size
+ * Supported dtypes as for decode.  No workspace.
+ * ------------------------------------------------------------------------ */
+pkv_status pkv_paged_attn_chunked_prefill(const pkv_cache_desc* cache,
+                                          const void* q, int32_t q_dtype,
+                                          void* out, int32_t out_dtype, float* lse,
+                                          const int32_t* cu_q_lens, const int32_t* ctx_before,
+                                          const int32_t* block_tables, int32_t bt_stride,
+                                          int32_t num_reqs, int32_t num_q_tokens,
+                                          int32_t num_q_heads, int32_t max_chunk_len,
+                                          float sm_scale, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * Utilities
+ * ------------------------------------------------------------------------ */
+
+/* Debug check, synchronous on `stream`: copies block_tables and lens to the
+ * host and checks 0 <= lens[s] <= bt_stride * page_size and that every entry
+ * covering tokens 0..lens[s]-1 is in [0, num_pages).  PKV_ERR_BAD_BLOCK_TABLE
+ * names the first offending row.  Device pointers; lens is int32[num_seqs]. */
+pkv_status pkv_validate_block_tables(const pkv_cache_desc* cache, const int32_t* block_tables,
+                                     int32_t bt_stride, const int32_t* lens, int32_t num_seqs,
+                                     void* stream);
+
+/* Decode n fp8 e4m3fn codes (device uint8[n]) to float (device float[n]) with
+ * the same device conversion the attention kernels use. */
+pkv_status pkv_fp8_e4m3fn_to_f32(const uint8_t* codes, float* out, int64_t n, void* stream);
+
+#ifdef __cplusplus
+}  /* extern "C" */
+#endif
+
+#endif  /* PAGEDKV_H_ */

@@ -1,0 +1,338 @@
+"""Python binding of the C ABI in ``include/pagedkv.h`` (ctypes).
+
+Argument marshalling only: every function here checks that tensors have the
+layout the C call documents, passes raw device pointers, sizes and the current
+HIP stream to ``libpagedkv.so``, and raises ``PkvError`` on a non-OK status.
+Every step of the computation runs in the library's HIP kernels.  PyTorch
+supplies device memory and streams.
+
+The library is loaded from the package directory (built in-tree by
+``python -m paged_kv_cache_277_amd.build``); if it is missing the import
+fails with an error that says so — there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
+
+PKV_OK, PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_OUT_OF_PAGES, \
+    PKV_ERR_BAD_BLOCK_TABLE, PKV_ERR_HIP = range(6)
+PKV_F32, PKV_BF16, PKV_FP8_E4M3FN = 0, 1, 2
+_STATUS_NAMES = {0: "PKV_OK", 1: "PKV_ERR_INVALID_ARG", 2: "PKV_ERR_UNSUPPORTED",
+                 3: "PKV_ERR_OUT_OF_PAGES", 4: "PKV_ERR_BAD_BLOCK_TABLE", 5: "PKV_ERR_HIP"}
+DTYPE_CODES = {"f32": PKV_F32, "bf16": PKV_BF16, "fp8": PKV_FP8_E4M3FN}
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+class CacheDescStruct(C.Structure):
+    _fields_ = [("k_pool", C.c_void_p), ("v_pool", C.c_void_p),
+                ("k_scale", C.c_void_p), ("v_scale", C.c_void_p),
+                ("num_pages", C.c_int32), ("num_kv_heads", C.c_int32),
+                ("page_size", C.c_int32), ("head_dim", C.c_int32), ("kv_dtype", C.c_int32)]
+
+
+_P = C.c_void_p
+_I = C.c_int32
+_F = C.c_float
+_SZ = C.c_size_t
+_SIGS = {
+    "pkv_version": (C.c_char_p, []),
+    "pkv_last_error": (C.c_char_p, []),
+    "pkv_allocator_create": (_I, [_I, C.POINTER(C.c_void_p)]),
+    "pkv_allocator_destroy": (None, [_P]),
+    "pkv_alloc_pages": (_I, [_P, _I, _P]),
+    "pkv_share_pages": (_I, [_P, _I, _P]),
+    "pkv_free_pages": (_I, [_P, _I, _P]),
+    "pkv_num_free_pages": (_I, [_P]),
+    "pkv_page_refcount": (_I, [_P, _I]),
+    "pkv_kv_cache_append": (_I, [_P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _P]),
+    "pkv_decode_split_tokens": (_I, [_P, _I, _I, _I]),
+    "pkv_decode_workspace_bytes": (_SZ, [_P, _I, _I, _I, _I]),
+    "pkv_paged_attn_decode": (_I, [_P, _P, _I, _P, _I, _P, _P, _I, _P, _I, _I, _I, _F, _I, _P, _SZ, _P]),
+    "pkv_paged_attn_decode_partial": (_I, [_P, _P, _I, _P, _I, _P, _P, _I, _P, _I, _I, _I, _F, _I, _P, _SZ, _P]),
+    "pkv_lse_merge": (_I, [_P, _P, _I, _P, _P, _I, _I, _I, _I, _P, _SZ, _P]),
+    "pkv_paged_attn_chunked_prefill": (_I, [_P, _P, _I, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
+    "pkv_validate_block_tables": (_I, [_P, _P, _I, _P, _I, _P]),
+    "pkv_fp8_e4m3fn_to_f32": (_I, [_P, _P, C.c_int64, _P]),
+}
+EXPORTED = tuple(_SIGS)
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    """The loaded library (loads it on first use; raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m paged_kv_cache_277_amd.build` (no fallback exists)")
+        h = C.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(h, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = h
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != PKV_OK:
+        raise PkvError(status, lib().pkv_last_error().decode(errors="replace"))
+
+
+def version() -> str:
+    return lib().pkv_version().decode()
+
+
+# ------------------------------------------------------------ helpers -------
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _need(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def _code_of(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return PKV_F32
+    if t.dtype == torch.bfloat16:
+        return PKV_BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return PKV_FP8_E4M3FN
+    raise ValueError(f"unsupported tensor dtype {t.dtype}")
+
+
+def _i32(t: torch.Tensor, name: str) -> None:
+    _need(t.dtype == torch.int32 and t.is_contiguous(), f"{name} must be contiguous int32")
+
+
+@dataclass
+class PagedCache:
+    """One layer's paged cache: K/V pools [num_pages][Hkv][page][D] on the device.
+
+    fp8 pools are uint8 (or float8_e4m3fn) tensors with float32 per-head scales."""
+    k_pool: torch.Tensor
+    v_pool: torch.Tensor
+    k_scale: Optional[torch.Tensor] = None
+    v_scale: Optional[torch.Tensor] = None
+
+    def __post_init__(self):
+        _need(self.k_pool.shape == self.v_pool.shape and self.k_pool.dim() == 4,
+              "k_pool/v_pool must both be [num_pages][Hkv][page][D]")
+        _need(self.k_pool.dtype == self.v_pool.dtype, "k_pool/v_pool dtypes differ")
+        _need(self.k_pool.is_contiguous() and self.v_pool.is_contiguous(), "pools must be contiguous")
+        for s in (self.k_scale, self.v_scale):
+            if s is not None:
+                _need(s.dtype == torch.float32 and s.is_contiguous(), "scales must be float32")
+        n, h, p, d = self.k_pool.shape
+        self._s = CacheDescStruct(_ptr(self.k_pool), _ptr(self.v_pool), _ptr(self.k_scale),
+                                  _ptr(self.v_scale), n, h, p, d, _code_of(self.k_pool))
+
+    @property
+    def num_pages(self) -> int: return self.k_pool.shape[0]
+    @property
+    def num_kv_heads(self) -> int: return self.k_pool.shape[1]
+    @property
+    def page_size(self) -> int: return self.k_pool.shape[2]
+    @property
+    def head_dim(self) -> int: return self.k_pool.shape[3]
+    @property
+    def kv_dtype(self) -> int: return self._s.kv_dtype
+
+    @property
+    def desc(self):
+        return C.byref(self._s)
+
+
+# ---------------------------------------------------------- allocator -------
+class PageAllocator:
+    """Host page allocator (refcounted; all-or-nothing allocation)."""
+
+    def __init__(self, num_pages: int):
+        h = C.c_void_p()
+        _check(lib().pkv_allocator_create(num_pages, C.byref(h)))
+        self._h = h
+
+    def close(self):
+        if self._h:
+            lib().pkv_allocator_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def alloc(self, n: int) -> list:
+        out = (C.c_int32 * max(1, n))()
+        _check(lib().pkv_alloc_pages(self._h, n, out))
+        return list(out[:n])
+
+    def share(self, ids) -> None:
+        arr = (C.c_int32 * max(1, len(ids)))(*ids)
+        _check(lib().pkv_share_pages(self._h, len(ids), arr))
+
+    def free(self, ids) -> None:
+        arr = (C.c_int32 * max(1, len(ids)))(*ids)
+        _check(lib().pkv_free_pages(self._h, len(ids), arr))
+
+    @property
+    def num_free(self) -> int:
+        return lib().pkv_num_free_pages(self._h)
+
+    def refcount(self, page: int) -> int:
+        return lib().pkv_page_refcount(self._h, page)
+
+
+# ------------------------------------------------------------- kernels ------
+def pkv_kv_cache_append(cache: PagedCache, k_new: torch.Tensor, v_new: torch.Tensor,
+                        cu_new_tokens: torch.Tensor, start_pos: torch.Tensor,
+                        block_tables: torch.Tensor, stream=None) -> None:
+    """Scatter packed new tokens [T][Hkv][D] into their page slots."""
+    _need(k_new.shape == v_new.shape and k_new.dim() == 3, "k_new/v_new must be [T][Hkv][D]")
+    _need(k_new.is_contiguous() and v_new.is_contiguous(), "k_new/v_new must be contiguous")
+    _need(k_new.shape[1:] == (cache.num_kv_heads, cache.head_dim), "k_new shape mismatch")
+    for t, n in ((cu_new_tokens, "cu_new_tokens"), (start_pos, "start_pos"),
+                 (block_tables, "block_tables")):
+        _i32(t, n)
+    rows = start_pos.shape[0]
+    _need(cu_new_tokens.shape[0] == rows + 1 and block_tables.shape[0] == rows, "row counts differ")
+    _check(lib().pkv_kv_cache_append(cache.desc, _ptr(k_new), _ptr(v_new), _code_of(k_new),
+                                     _ptr(cu_new_tokens), _ptr(start_pos), _ptr(block_tables),
+                                     block_tables.shape[1] if block_tables.dim() == 2 else 0,
+                                     rows, k_new.shape[0], _stream(stream)))
+
+
+def pkv_decode_split_tokens(cache: PagedCache, num_seqs: int, num_q_heads: int,
+                            max_context_len: int) -> int:
+    return lib().pkv_decode_split_tokens(cache.desc, num_seqs, num_q_heads, max_context_len)
+
+
+def pkv_decode_workspace_bytes(cache: PagedCache, num_seqs: int, num_q_heads: int,
+                               max_context_len: int, split_tokens: int = 0) -> int:
+    return lib().pkv_decode_workspace_bytes(cache.desc, num_seqs, num_q_heads, max_context_len,
+                                            split_tokens)
+
+
+def decode_workspace(cache: PagedCache, num_seqs: int, num_q_heads: int, max_context_len: int,
+                     split_tokens: int = 0) -> Optional[torch.Tensor]:
+    """A device buffer of the size the decode call needs (None if it needs none)."""
+    n = pkv_decode_workspace_bytes(cache, num_seqs, num_q_heads, max_context_len, split_tokens)
+    if n == 0:
+        return None
+    return torch.empty(n, dtype=torch.uint8, device=cache.k_pool.device)
+
+
+def _decode_args(cache, q, out, lse, block_tables, context_lens):
+    _need(q.dim() == 3 and q.is_contiguous(), "q must be contiguous [B][Hq][D]")
+    _need(out.shape == q.shape and out.is_contiguous(), "out must be contiguous like q")
+    _i32(block_tables, "block_tables")
+    _i32(context_lens, "context_lens")
+    _need(block_tables.dim() == 2 and block_tables.shape[0] == q.shape[0], "block_tables rows")
+    _need(context_lens.shape[0] == q.shape[0], "context_lens length")
+    if lse is not None:
+        _need(lse.dtype == torch.float32 and lse.shape == q.shape[:2] and lse.is_contiguous(),
+              "lse must be float32 [B][Hq]")
+
+
+def _ws(workspace):
+    if workspace is None:
+        return None, 0
+    return _ptr(workspace), workspace.numel() * workspace.element_size()
+
+
+def pkv_paged_attn_decode(cache: PagedCache, q: torch.Tensor, out: torch.Tensor,
+                          block_tables: torch.Tensor, context_lens: torch.Tensor,
+                          max_context_len: int, sm_scale: float, lse: Optional[torch.Tensor] = None,
+                          split_tokens: int = 0, workspace: Optional[torch.Tensor] = None,
+                          stream=None) -> None:
+    """Decode attention (partial pass + log-sum-exp merge)."""
+    _decode_args(cache, q, out, lse, block_tables, context_lens)
+    wp, wb = _ws(workspace)
+    _check(lib().pkv_paged_attn_decode(cache.desc, _ptr(q), _code_of(q), _ptr(out), _code_of(out),
+                                       _ptr(lse), _ptr(block_tables), block_tables.shape[1],
+                                       _ptr(context_lens), q.shape[0], q.shape[1], max_context_len,
+                                       float(sm_scale), split_tokens, wp, wb, _stream(stream)))
+
+
+def pkv_paged_attn_decode_partial(cache: PagedCache, q: torch.Tensor, out: torch.Tensor,
+                                  block_tables: torch.Tensor, context_lens: torch.Tensor,
+                                  max_context_len: int, sm_scale: float,
+                                  lse: Optional[torch.Tensor] = None, split_tokens: int = 0,
+                                  workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    _decode_args(cache, q, out, lse, block_tables, context_lens)
+    wp, wb = _ws(workspace)
+    _check(lib().pkv_paged_attn_decode_partial(
+        cache.desc, _ptr(q), _code_of(q), _ptr(out), _code_of(out), _ptr(lse), _ptr(block_tables),
+        block_tables.shape[1], _ptr(context_lens), q.shape[0], q.shape[1], max_context_len,
+        float(sm_scale), split_tokens, wp, wb, _stream(stream)))
+
+
+def pkv_lse_merge(cache: PagedCache, out: torch.Tensor, context_lens: torch.Tensor,
+                  max_context_len: int, lse: Optional[torch.Tensor] = None, split_tokens: int = 0,
+                  workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    _i32(context_lens, "context_lens")
+    wp, wb = _ws(workspace)
+    _check(lib().pkv_lse_merge(cache.desc, _ptr(out), _code_of(out), _ptr(lse), _ptr(context_lens),
+                               out.shape[0], out.shape[1], max_context_len, split_tokens, wp, wb,
+                               _stream(stream)))
+
+
+def pkv_paged_attn_chunked_prefill(cache: PagedCache, q: torch.Tensor, out: torch.Tensor,
+                                   cu_q_lens: torch.Tensor, ctx_before: torch.Tensor,
+                                   block_tables: torch.Tensor, max_chunk_len: int,
+                                   sm_scale: float, lse: Optional[torch.Tensor] = None,
+                                   stream=None) -> None:
+    """Causal chunked prefill over packed query rows [T][Hq][D]."""
+    _need(q.dim() == 3 and q.is_contiguous(), "q must be contiguous [T][Hq][D]")
+    _need(out.shape == q.shape and out.is_contiguous(), "out must be contiguous like q")
+    for t, n in ((cu_q_lens, "cu_q_lens"), (ctx_before, "ctx_before"),
+                 (block_tables, "block_tables")):
+        _i32(t, n)
+    R = ctx_before.shape[0]
+    _need(cu_q_lens.shape[0] == R + 1 and block_tables.shape[0] == R, "request counts differ")
+    if lse is not None:
+        _need(lse.dtype == torch.float32 and lse.shape == q.shape[:2] and lse.is_contiguous(),
+              "lse must be float32 [T][Hq]")
+    _check(lib().pkv_paged_attn_chunked_prefill(
+        cache.desc, _ptr(q), _code_of(q), _ptr(out), _code_of(out), _ptr(lse), _ptr(cu_q_lens),
+        _ptr(ctx_before), _ptr(block_tables), block_tables.shape[1], R, q.shape[0], q.shape[1],
+        max_chunk_len, float(sm_scale), _stream(stream)))
+
+
+def pkv_validate_block_tables(cache: PagedCache, block_tables: torch.Tensor, lens: torch.Tensor,
+                              stream=None) -> None:
+    _i32(block_tables, "block_tables")
+    _i32(lens, "lens")
+    _check(lib().pkv_validate_block_tables(cache.desc, _ptr(block_tables), block_tables.shape[1],
+                                           _ptr(lens), lens.shape[0], _stream(stream)))
+
+
+def pkv_fp8_e4m3fn_to_f32(codes: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+    _need(codes.dtype in (torch.uint8, torch.float8_e4m3fn) and codes.is_contiguous(), "codes")
+    _need(out.dtype == torch.float32 and out.numel() == codes.numel(), "out")
+    _check(lib().pkv_fp8_e4m3fn_to_f32(_ptr(codes), _ptr(out), codes.numel(), _stream(stream)))

@@ -1,0 +1,387 @@
+// C ABI front end: argument checks, split planning, workspace carving,
+// launches.  Nothing here touches the device before every host-side check
+// has passed, so a failing call enqueues nothing.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <limits>
+#include <string>
+#include <vector>
+
+#include "../../include/pagedkv.h"
+#include "pkv_launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+pkv_status fail(pkv_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+pkv_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return PKV_OK;
+  return fail(PKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int kNumCUs = 256;          // MI355X compute units
+constexpr int kMaxGridYZ = 65535;
+
+pkv_status check_cache(const pkv_cache_desc* c) {
+  if (!c) return fail(PKV_ERR_INVALID_ARG, "cache descriptor is NULL");
+  if (!c->k_pool || !c->v_pool) return fail(PKV_ERR_INVALID_ARG, "k_pool/v_pool is NULL");
+  if (c->num_pages <= 0 || c->num_kv_heads <= 0)
+    return fail(PKV_ERR_INVALID_ARG, "num_pages (%d) and num_kv_heads (%d) must be positive",
+                c->num_pages, c->num_kv_heads);
+  if (c->kv_dtype < PKV_F32 || c->kv_dtype > PKV_FP8_E4M3FN)
+    return fail(PKV_ERR_INVALID_ARG, "kv_dtype %d is not a pkv_dtype", c->kv_dtype);
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", c->head_dim);
+  if (c->page_size != 16 && c->page_size != 32 && c->page_size != 64)
+    return fail(PKV_ERR_UNSUPPORTED, "page_size %d (supported: 16, 32, 64)", c->page_size);
+  if (c->kv_dtype == PKV_FP8_E4M3FN && (!c->k_scale || !c->v_scale))
+    return fail(PKV_ERR_INVALID_ARG, "fp8 cache needs k_scale and v_scale");
+  if (c->kv_dtype != PKV_FP8_E4M3FN && (c->k_scale || c->v_scale))
+    return fail(PKV_ERR_INVALID_ARG, "k_scale/v_scale are only for an fp8 cache");
+  return PKV_OK;
+}
+
+pkv_status check_qo_dtypes(const pkv_cache_desc* c, int32_t q_dtype, int32_t out_dtype) {
+  const bool ok = (c->kv_dtype == PKV_F32 && q_dtype == PKV_F32 && out_dtype == PKV_F32) ||
+                  (c->kv_dtype == PKV_BF16 && q_dtype == PKV_BF16 && out_dtype == PKV_BF16) ||
+                  (c->kv_dtype == PKV_FP8_E4M3FN && q_dtype == PKV_BF16 && out_dtype == PKV_BF16);
+  if (!ok)
+    return fail(PKV_ERR_UNSUPPORTED, "dtype combination q=%d kv=%d out=%d not supported", q_dtype,
+                c->kv_dtype, out_dtype);
+  return PKV_OK;
+}
+
+pkv_status check_heads(const pkv_cache_desc* c, int32_t num_q_heads) {
+  if (num_q_heads <= 0 || num_q_heads % c->num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID_ARG, "num_q_heads %d is not a positive multiple of num_kv_heads %d",
+                num_q_heads, c->num_kv_heads);
+  const int G = num_q_heads / c->num_kv_heads;
+  if (G > 16) return fail(PKV_ERR_UNSUPPORTED, "query group size %d > 16", G);
+  if (c->num_kv_heads > kMaxGridYZ) return fail(PKV_ERR_UNSUPPORTED, "too many KV heads");
+  return PKV_OK;
+}
+
+pkv::CacheView view(const pkv_cache_desc* c) {
+  pkv::CacheView v;
+  v.k_pool = c->k_pool;
+  v.v_pool = c->v_pool;
+  v.k_pool_w = c->k_pool;
+  v.v_pool_w = c->v_pool;
+  v.k_scale = c->k_scale;
+  v.v_scale = c->v_scale;
+  v.num_pages = c->num_pages;
+  v.num_kv_heads = c->num_kv_heads;
+  v.page_size = c->page_size;
+  v.head_dim = c->head_dim;
+  v.kv_dtype = c->kv_dtype;
+  return v;
+}
+
+int32_t ceil_div(int64_t a, int64_t b) { return (int32_t)((a + b - 1) / b); }
+
+int32_t default_split(const pkv_cache_desc* c, int32_t num_seqs, int32_t max_len) {
+  // A work item reads about 256 KiB of K+V per KV head by default (512 tokens
+  // of 16-bit or 1024 of fp8 at head_dim 128); smaller ranges are used when
+  // the batch would otherwise give fewer than ~8 work items per CU.
+  const int gran = std::max(16, (int)c->page_size);
+  int split = c->kv_dtype == PKV_FP8_E4M3FN ? 1024 : 512;
+  if (c->head_dim == 64) split *= 2;
+  split = std::max(gran, split / gran * gran);
+  const int64_t pairs = (int64_t)std::max(1, num_seqs) * c->num_kv_heads;
+  while (split > 2 * gran && pairs * ceil_div(std::max(1, max_len), split) < 8 * kNumCUs)
+    split = std::max(gran, split / 2 / gran * gran);
+  if (max_len <= split) split = std::max(gran, ceil_div(std::max(1, max_len), gran) * gran);
+  return split;
+}
+
+pkv_status resolve_split(const pkv_cache_desc* c, int32_t num_seqs, int32_t max_len,
+                         int32_t split_tokens, int32_t* out) {
+  if (split_tokens == 0) {
+    *out = default_split(c, num_seqs, max_len);
+    return PKV_OK;
+  }
+  if (split_tokens < 0 || split_tokens % c->page_size != 0 || split_tokens % 16 != 0)
+    return fail(PKV_ERR_INVALID_ARG, "split_tokens %d must be a positive multiple of page_size %d",
+                split_tokens, c->page_size);
+  *out = split_tokens;
+  return PKV_OK;
+}
+
+size_t workspace_bytes(const pkv_cache_desc* c, int32_t num_seqs, int32_t num_q_heads,
+                       int32_t max_len, int32_t split) {
+  const int32_t ms = ceil_div(std::max(0, max_len), split);
+  if (ms <= 1 || num_seqs <= 0) return 0;
+  // acc [rows][Hq][ms][D] + (m, l) [rows][Hq][ms][2], float32, each 256-byte aligned
+  const size_t n = (size_t)num_seqs * num_q_heads * ms;
+  const size_t acc = (n * c->head_dim * 4 + 255) / 256 * 256;
+  const size_t ml = (n * 2 * 4 + 255) / 256 * 256;
+  return acc + ml;
+}
+
+struct DecodeSetup {
+  pkv::AttnArgs a;
+};
+
+pkv_status prepare_decode(const pkv_cache_desc* cache, const void* q, int32_t q_dtype, void* out,
+                          int32_t out_dtype, float* lse, const int32_t* block_tables,
+                          int32_t bt_stride, const int32_t* context_lens, int32_t num_seqs,
+                          int32_t num_q_heads, int32_t max_context_len, float sm_scale,
+                          int32_t split_tokens, const void* workspace, size_t workspace_bytes_in,
+                          bool need_q, pkv::AttnArgs* a) {
+  pkv_status st;
+  if ((st = check_cache(cache)) != PKV_OK) return st;
+  if ((st = check_qo_dtypes(cache, q_dtype, out_dtype)) != PKV_OK) return st;
+  if ((st = check_heads(cache, num_q_heads)) != PKV_OK) return st;
+  if (num_seqs < 0 || max_context_len < 0)
+    return fail(PKV_ERR_INVALID_ARG, "num_seqs %d / max_context_len %d negative", num_seqs,
+                max_context_len);
+  if (num_seqs > kMaxGridYZ) return fail(PKV_ERR_UNSUPPORTED, "num_seqs %d > %d", num_seqs, kMaxGridYZ);
+  if (num_seqs > 0) {
+    if ((need_q && !q) || !out || !context_lens || (need_q && !block_tables))
+      return fail(PKV_ERR_INVALID_ARG, "q/out/block_tables/context_lens must not be NULL");
+    if (need_q && bt_stride <= 0) return fail(PKV_ERR_INVALID_ARG, "bt_stride %d", bt_stride);
+    if (need_q && (int64_t)bt_stride * cache->page_size < max_context_len)
+      return fail(PKV_ERR_INVALID_ARG, "max_context_len %d exceeds bt_stride*page_size %lld",
+                  max_context_len, (long long)bt_stride * cache->page_size);
+  }
+  if (!std::isfinite(sm_scale)) return fail(PKV_ERR_INVALID_ARG, "sm_scale is not finite");
+  int32_t split;
+  if ((st = resolve_split(cache, num_seqs, max_context_len, split_tokens, &split)) != PKV_OK)
+    return st;
+  const size_t need = workspace_bytes(cache, num_seqs, num_q_heads, max_context_len, split);
+  if (need > 0 && (!workspace || workspace_bytes_in < need))
+    return fail(PKV_ERR_INVALID_ARG, "workspace of %zu bytes needed, %zu given", need,
+                workspace_bytes_in);
+  const int32_t ms = std::max(1, ceil_div(std::max(0, max_context_len), split));
+  std::memset(a, 0, sizeof *a);
+  a->c = view(cache);
+  a->q = q;
+  a->out = out;
+  a->lse = lse;
+  a->bt = block_tables;
+  a->bt_stride = bt_stride;
+  a->context_lens = context_lens;
+  a->num_rows = num_seqs;
+  a->num_q_heads = num_q_heads;
+  a->split_tokens = split;
+  a->max_splits = ms;
+  a->sm_scale = sm_scale;
+  if (need > 0) {
+    char* w = static_cast<char*>(const_cast<void*>(workspace));
+    const size_t n = (size_t)num_seqs * num_q_heads * ms;
+    a->ws_acc = reinterpret_cast<float*>(w);
+    a->ws_ml = reinterpret_cast<float*>(w + (n * cache->head_dim * 4 + 255) / 256 * 256);
+  }
+  return PKV_OK;
+}
+
+}  // namespace
+
+namespace pkv_detail {
+void set_error(const std::string& s) { g_err = s; }
+}  // namespace pkv_detail
+
+extern "C" {
+
+const char* pkv_version(void) { return "0.1.0"; }
+
+const char* pkv_last_error(void) { return g_err.c_str(); }
+
+pkv_status pkv_kv_cache_append(const pkv_cache_desc* cache, const void* k_new, const void* v_new,
+                               int32_t in_dtype, const int32_t* cu_new_tokens,
+                               const int32_t* start_pos, const int32_t* block_tables,
+                               int32_t bt_stride, int32_t num_rows, int32_t num_new_tokens,
+                               void* stream) {
+  pkv_status st;
+  if ((st = check_cache(cache)) != PKV_OK) return st;
+  const int32_t want_in = cache->kv_dtype == PKV_FP8_E4M3FN ? PKV_F32 : cache->kv_dtype;
+  if (in_dtype != want_in)
+    return fail(PKV_ERR_UNSUPPORTED, "append into kv_dtype %d takes in_dtype %d, got %d",
+                cache->kv_dtype, want_in, in_dtype);
+  if (num_rows < 0 || num_new_tokens < 0)
+    return fail(PKV_ERR_INVALID_ARG, "num_rows %d / num_new_tokens %d negative", num_rows,
+                num_new_tokens);
+  if (num_new_tokens > 0) {
+    if (num_rows == 0) return fail(PKV_ERR_INVALID_ARG, "tokens given but no rows");
+    if (!k_new || !v_new || !cu_new_tokens || !start_pos || !block_tables)
+      return fail(PKV_ERR_INVALID_ARG, "append pointers must not be NULL");
+    if (bt_stride <= 0) return fail(PKV_ERR_INVALID_ARG, "bt_stride %d", bt_stride);
+  }
+  pkv::AppendArgs a;
+  a.c = view(cache);
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.in_dtype = in_dtype;
+  a.cu = cu_new_tokens;
+  a.start_pos = start_pos;
+  a.bt = block_tables;
+  a.bt_stride = bt_stride;
+  a.num_rows = num_rows;
+  a.num_tokens = num_new_tokens;
+  return hip_status(pkv::launch_append(a, static_cast<hipStream_t>(stream)), "kv_cache_append");
+}
+
+int32_t pkv_decode_split_tokens(const pkv_cache_desc* cache, int32_t num_seqs, int32_t num_q_heads,
+                                int32_t max_context_len) {
+  if (check_cache(cache) != PKV_OK || check_heads(cache, num_q_heads) != PKV_OK) return 0;
+  if (num_seqs < 0 || max_context_len < 0) return 0;
+  return default_split(cache, num_seqs, max_context_len);
+}
+
+size_t pkv_decode_workspace_bytes(const pkv_cache_desc* cache, int32_t num_seqs,
+                                  int32_t num_q_heads, int32_t max_context_len,
+                                  int32_t split_tokens) {
+  if (check_cache(cache) != PKV_OK || check_heads(cache, num_q_heads) != PKV_OK) return 0;
+  int32_t split;
+  if (resolve_split(cache, num_seqs, max_context_len, split_tokens, &split) != PKV_OK) return 0;
+  return workspace_bytes(cache, num_seqs, num_q_heads, max_context_len, split);
+}
+
+pkv_status pkv_paged_attn_decode_partial(const pkv_cache_desc* cache, const void* q,
+                                         int32_t q_dtype, void* out, int32_t out_dtype, float* lse,
+                                         const int32_t* block_tables, int32_t bt_stride,
+                                         const int32_t* context_lens, int32_t num_seqs,
+                                         int32_t num_q_heads, int32_t max_context_len,
+                                         float sm_scale, int32_t split_tokens, void* workspace,
+                                         size_t workspace_bytes_in, void* stream) {
+  pkv::AttnArgs a;
+  pkv_status st = prepare_decode(cache, q, q_dtype, out, out_dtype, lse, block_tables, bt_stride,
+                                 context_lens, num_seqs, num_q_heads, max_context_len, sm_scale,
+                                 split_tokens, workspace, workspace_bytes_in, true, &a);
+  if (st != PKV_OK) return st;
+  return hip_status(pkv::launch_decode_partial(a, static_cast<hipStream_t>(stream)),
+                    "paged_attn_decode (partial)");
+}
+
+pkv_status pkv_lse_merge(const pkv_cache_desc* cache, void* out, int32_t out_dtype, float* lse,
+                         const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                         int32_t max_context_len, int32_t split_tokens, const void* workspace,
+                         size_t workspace_bytes_in, void* stream) {
+  pkv::AttnArgs a;
+  const int32_t q_dtype = cache && cache->kv_dtype == PKV_F32 ? PKV_F32 : PKV_BF16;
+  pkv_status st = prepare_decode(cache, nullptr, q_dtype, out, out_dtype, lse, nullptr, 0,
+                                 context_lens, num_seqs, num_q_heads, max_context_len, 1.0f,
+                                 split_tokens, workspace, workspace_bytes_in, false, &a);
+  if (st != PKV_OK) return st;
+  return hip_status(pkv::launch_lse_merge(a, static_cast<hipStream_t>(stream)), "lse_merge");
+}
+
+pkv_status pkv_paged_attn_decode(const pkv_cache_desc* cache, const void* q, int32_t q_dtype,
+                                 void* out, int32_t out_dtype, float* lse,
+                                 const int32_t* block_tables, int32_t bt_stride,
+                                 const int32_t* context_lens, int32_t num_seqs,
+                                 int32_t num_q_heads, int32_t max_context_len, float sm_scale,
+                                 int32_t split_tokens, void* workspace, size_t workspace_bytes_in,
+                                 void* stream) {
+  pkv::AttnArgs a;
+  pkv_status st = prepare_decode(cache, q, q_dtype, out, out_dtype, lse, block_tables, bt_stride,
+                                 context_lens, num_seqs, num_q_heads, max_context_len, sm_scale,
+                                 split_tokens, workspace, workspace_bytes_in, true, &a);
+  if (st != PKV_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = hip_status(pkv::launch_decode_partial(a, s), "paged_attn_decode (partial)")) != PKV_OK)
+    return st;
+  return hip_status(pkv::launch_lse_merge(a, s), "paged_attn_decode (merge)");
+}
+
+pkv_status pkv_paged_attn_chunked_prefill(const pkv_cache_desc* cache, const void* q,
+                                          int32_t q_dtype, void* out, int32_t out_dtype,
+                                          float* lse, const int32_t* cu_q_lens,
+                                          const int32_t* ctx_before, const int32_t* block_tables,
+                                          int32_t bt_stride, int32_t num_reqs,
+                                          int32_t num_q_tokens, int32_t num_q_heads,
+                                          int32_t max_chunk_len, float sm_scale, void* stream) {
+  pkv_status st;
+  if ((st = check_cache(cache)) != PKV_OK) return st;
+  if ((st = check_qo_dtypes(cache, q_dtype, out_dtype)) != PKV_OK) return st;
+  if ((st = check_heads(cache, num_q_heads)) != PKV_OK) return st;
+  if (num_reqs < 0 || num_q_tokens < 0 || max_chunk_len < 0)
+    return fail(PKV_ERR_INVALID_ARG, "negative size");
+  if (!std::isfinite(sm_scale)) return fail(PKV_ERR_INVALID_ARG, "sm_scale is not finite");
+  if (num_q_tokens == 0 || num_reqs == 0) return PKV_OK;
+  if (!q || !out || !cu_q_lens || !ctx_before || !block_tables)
+    return fail(PKV_ERR_INVALID_ARG, "prefill pointers must not be NULL");
+  if (bt_stride <= 0) return fail(PKV_ERR_INVALID_ARG, "bt_stride %d", bt_stride);
+  if (max_chunk_len <= 0) return fail(PKV_ERR_INVALID_ARG, "max_chunk_len must be positive");
+  if ((int64_t)num_reqs * max_chunk_len > kMaxGridYZ)
+    return fail(PKV_ERR_UNSUPPORTED, "num_reqs * max_chunk_len > %d", kMaxGridYZ);
+  pkv::AttnArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.c = view(cache);
+  a.q = q;
+  a.out = out;
+  a.lse = lse;
+  a.bt = block_tables;
+  a.bt_stride = bt_stride;
+  a.cu_q = cu_q_lens;
+  a.ctx_before = ctx_before;
+  a.num_rows = num_reqs;
+  a.max_chunk = max_chunk_len;
+  a.num_q_heads = num_q_heads;
+  const int64_t cap = (int64_t)bt_stride * cache->page_size;
+  a.split_tokens = (int32_t)std::min<int64_t>((cap + 15) / 16 * 16, (int64_t)1 << 30);
+  a.max_splits = 1;
+  a.sm_scale = sm_scale;
+  a.prefill = 1;
+  return hip_status(pkv::launch_prefill(a, static_cast<hipStream_t>(stream)),
+                    "paged_attn_chunked_prefill");
+}
+
+pkv_status pkv_validate_block_tables(const pkv_cache_desc* cache, const int32_t* block_tables,
+                                     int32_t bt_stride, const int32_t* lens, int32_t num_seqs,
+                                     void* stream) {
+  pkv_status st;
+  if ((st = check_cache(cache)) != PKV_OK) return st;
+  if (num_seqs < 0 || bt_stride <= 0) return fail(PKV_ERR_INVALID_ARG, "num_seqs/bt_stride");
+  if (num_seqs == 0) return PKV_OK;
+  if (!block_tables || !lens) return fail(PKV_ERR_INVALID_ARG, "NULL block_tables/lens");
+  std::vector<int32_t> bt((size_t)num_seqs * bt_stride), ln(num_seqs);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = hip_status(hipMemcpyAsync(bt.data(), block_tables, bt.size() * 4, hipMemcpyDeviceToHost, s),
+                       "validate: copy block tables")) != PKV_OK)
+    return st;
+  if ((st = hip_status(hipMemcpyAsync(ln.data(), lens, ln.size() * 4, hipMemcpyDeviceToHost, s),
+                       "validate: copy lengths")) != PKV_OK)
+    return st;
+  if ((st = hip_status(hipStreamSynchronize(s), "validate: synchronize")) != PKV_OK) return st;
+  const int64_t cap = (int64_t)bt_stride * cache->page_size;
+  for (int32_t r = 0; r < num_seqs; ++r) {
+    if (ln[r] < 0 || ln[r] > cap)
+      return fail(PKV_ERR_BAD_BLOCK_TABLE, "row %d: length %d outside [0, %lld]", r, ln[r],
+                  (long long)cap);
+    const int32_t used = ceil_div(ln[r], cache->page_size);
+    for (int32_t i = 0; i < used; ++i) {
+      const int32_t id = bt[(size_t)r * bt_stride + i];
+      if (id < 0 || id >= cache->num_pages)
+        return fail(PKV_ERR_BAD_BLOCK_TABLE, "row %d: entry %d = %d outside [0, %d)", r, i, id,
+                    cache->num_pages);
+    }
+  }
+  return PKV_OK;
+}
+
+pkv_status pkv_fp8_e4m3fn_to_f32(const uint8_t* codes, float* out, int64_t n, void* stream) {
+  if (n < 0) return fail(PKV_ERR_INVALID_ARG, "n negative");
+  if (n > 0 && (!codes || !out)) return fail(PKV_ERR_INVALID_ARG, "NULL pointer");
+  if (n > 0 && (reinterpret_cast<uintptr_t>(codes) & 3))
+    return fail(PKV_ERR_INVALID_ARG, "codes must be 4-byte aligned");
+  return hip_status(pkv::launch_fp8_to_f32(codes, out, n, static_cast<hipStream_t>(stream)),
+                    "fp8_e4m3fn_to_f32");
+}
+
+}  // extern "C"

@@ -1,0 +1,109 @@
+// kv_cache_append: scatter new tokens' K/V rows into their page slots.
+//
+// A new token joins its request's cache at the next logical position; the
+// position maps to a physical page through the request's block table
+// ("TensorRT-LLM框架解析与高性能推理优化实践" §4.2; in-flight batching places each
+// request's KV as it grows, "TensorRT-LLM内核融合与动态批处理", In-flight Batching).
+// An fp8 cache stores x / scale[head] rounded to e4m3fn (first page, §7.2).
+//
+// Launch: one workgroup per new token; its threads cover the token's
+// Hkv x head_dim row in 16-byte output pieces, so every page row is written
+// with full 16-byte stores and the packed input is read contiguously.
+#include "pkv_device.h"
+#include "pkv_launch.h"
+
+namespace pkv {
+namespace {
+
+template <int KVT>
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+  constexpr int KVB = KvBytes<KVT>::value;
+  constexpr int EPL = 16 / KVB;                  // cache elements per 16-byte piece
+  const int t = blockIdx.x;
+  // Row r owning packed token t: the largest r with cu[r] <= t.
+  int lo = 0, hi = a.num_rows;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.cu[mid] <= t) lo = mid; else hi = mid;
+  }
+  const int r = lo;
+  const int pos = a.start_pos[r] + (t - a.cu[r]);
+  const int P = a.c.page_size;
+  const int page = a.bt[(size_t)r * a.bt_stride + pos / P];
+  const int slot = pos % P;
+  const int D = a.c.head_dim, Hkv = a.c.num_kv_heads;
+  const int pieces = D / EPL;                    // per head
+  const int total = Hkv * pieces;
+  uint8_t* kdst = static_cast<uint8_t*>(a.c.k_pool_w);
+  uint8_t* vdst = static_cast<uint8_t*>(a.c.v_pool_w);
+  for (int c = threadIdx.x; c < total; c += blockDim.x) {
+    const int j = c / pieces, pc = c % pieces;
+    const size_t dst = ((((size_t)page * Hkv + j) * P + slot) * D + (size_t)pc * EPL) * KVB;
+    const size_t src_e = ((size_t)t * Hkv + j) * D + (size_t)pc * EPL;   // input element
+    if constexpr (KVT == KV_FP8) {
+      // F32 input: 16 floats -> 16 codes.
+      const float ks = a.c.k_scale[j], vs = a.c.v_scale[j];
+      const u32x4* ksrc = reinterpret_cast<const u32x4*>(static_cast<const float*>(a.k_new) + src_e);
+      const u32x4* vsrc = reinterpret_cast<const u32x4*>(static_cast<const float*>(a.v_new) + src_e);
+      u32x4 ko, vo;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const u32x4 kx = ksrc[q4], vx = vsrc[q4];
+        uint32_t kw = 0, vw = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          kw |= f32_to_e4m3fn(__uint_as_float(kx[e]) / ks) << (8 * e);
+          vw |= f32_to_e4m3fn(__uint_as_float(vx[e]) / vs) << (8 * e);
+        }
+        ko[q4] = kw;
+        vo[q4] = vw;
+      }
+      *reinterpret_cast<u32x4*>(kdst + dst) = ko;
+      *reinterpret_cast<u32x4*>(vdst + dst) = vo;
+    } else {
+      const uint8_t* ks = static_cast<const uint8_t*>(a.k_new) + src_e * KVB;
+      const uint8_t* vs = static_cast<const uint8_t*>(a.v_new) + src_e * KVB;
+      *reinterpret_cast<u32x4*>(kdst + dst) = ld16(ks);
+      *reinterpret_cast<u32x4*>(vdst + dst) = ld16(vs);
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void fp8_to_f32_kernel(const uint8_t* codes, float* out, int64_t n) {
+  const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (i + 4 <= n) {
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(codes + i);
+    float o[4];
+    fp8x4_to_f32(w, o);
+    out[i] = o[0]; out[i + 1] = o[1]; out[i + 2] = o[2]; out[i + 3] = o[3];
+  } else if (i < n) {
+    uint32_t w = 0;
+    for (int64_t k = i; k < n; ++k) w |= uint32_t(codes[k]) << (8 * (k - i));
+    float o[4];
+    fp8x4_to_f32(w, o);
+    for (int64_t k = i; k < n; ++k) out[k] = o[k - i];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
+  if (a.num_tokens == 0) return hipSuccess;
+  const dim3 grid(a.num_tokens), block(a.c.num_kv_heads * a.c.head_dim >= 2048 ? 256 : 128);
+  switch (a.c.kv_dtype) {
+    case KV_F32: hipLaunchKernelGGL(append_kernel<KV_F32>, grid, block, 0, s, a); break;
+    case KV_BF16: hipLaunchKernelGGL(append_kernel<KV_BF16>, grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL(append_kernel<KV_FP8>, grid, block, 0, s, a); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_to_f32(const uint8_t* codes, float* out, int64_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const int64_t groups = (n + 3) / 4;
+  const dim3 grid((unsigned)((groups + 255) / 256)), block(256);
+  hipLaunchKernelGGL(fp8_to_f32_kernel, grid, block, 0, s, codes, out, n);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -1,0 +1,351 @@
+// Paged decode attention: split-K partial pass (vector path) and the
+// log-sum-exp merge.
+//
+// Method: the query attends every cached token of its sequence; the kernel
+// reaches each token's K/V through the block table (page = bt[t / P], slot
+// t % P) — "TensorRT-LLM框架解析与高性能推理优化实践" §6.2 — and keeps a running
+// max and running sum so that one pass over the keys gives the softmax
+// (§6.1).  The score is sm_scale * <q, k> (scaled dot-product attention,
+// "TensorRT-LLM性能调优：提升LLM推理效率", fused-MHA row of the layer-fusion table).
+//
+// Work decomposition (MI355X): one workgroup of 4 waves per
+// (row, KV head, context range of split_tokens tokens).  The G query heads
+// that share a KV head are processed together, so each K/V byte is read
+// once per group.  Within a wave, R = head_dim*bytes/16 consecutive lanes
+// read one token row with 16-byte loads (a wave reads 64/R whole rows per
+// instruction, contiguous inside the page), each lane dots its 16-byte piece
+// with the matching query slice and the R-lane group sums the pieces.
+// Every row-group of a wave runs its own online softmax; the states merge
+// across lanes and waves at the end.  Ranges are aligned to 16 tokens and
+// page sizes are multiples of 16, so every 16-token tile sits in one page
+// and costs one block-table read.
+//
+// Output of a work item: if the row needs one range, the final output and
+// log-sum-exp; otherwise (m, l, acc) into the workspace for the merge.
+// m is kept in the log2 domain (scores are pre-multiplied by log2(e)).
+#include <math.h>
+
+#include "pkv_device.h"
+#include "pkv_launch.h"
+
+namespace pkv {
+namespace {
+
+constexpr int kWaves = 4;
+
+template <int KVT, int D>
+struct VecShape {
+  static constexpr int KVB = KvBytes<KVT>::value;
+  static constexpr int EPL = 16 / KVB;                 // elements per lane load
+  static constexpr int R = D / EPL;                    // lanes per token row
+  static constexpr int RW = 64 / R;                    // rows per wave load
+  static constexpr int U = (16 / RW) < 4 ? (16 / RW) : 4;  // loads per lane per tile
+  static constexpr int TOK = U * RW;                   // tokens per wave tile
+  static_assert(R >= 1 && R <= 64 && U >= 1, "shape");
+};
+
+// Convert one 16-byte piece to floats.
+template <int KVT>
+__device__ __forceinline__ void piece_to_f32(const u32x4& x, float* o) {
+  if constexpr (KVT == KV_F32) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = __uint_as_float(x[i]);
+  } else if constexpr (KVT == KV_BF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { o[2 * i] = bf16_lo(x[i]); o[2 * i + 1] = bf16_hi(x[i]); }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fp8x4_to_f32(x[i], o + 4 * i);
+  }
+}
+
+template <typename T> __device__ __forceinline__ float load_q(const void* q, size_t i);
+template <> __device__ __forceinline__ float load_q<float>(const void* q, size_t i) {
+  return static_cast<const float*>(q)[i];
+}
+template <> __device__ __forceinline__ float load_q<uint16_t>(const void* q, size_t i) {
+  return bf16_to_f32(static_cast<const uint16_t*>(q)[i]);
+}
+
+template <typename T> __device__ __forceinline__ void store_o(void* o, size_t i, float v);
+template <> __device__ __forceinline__ void store_o<float>(void* o, size_t i, float v) {
+  static_cast<float*>(o)[i] = v;
+}
+template <> __device__ __forceinline__ void store_o<uint16_t>(void* o, size_t i, float v) {
+  static_cast<uint16_t*>(o)[i] = f32_to_bf16_rne(v);
+}
+
+// Resolve which query row, context length and block-table row a launch row
+// (blockIdx.z) stands for.  Returns false if the row is empty padding.
+__device__ __forceinline__ bool resolve_row(const AttnArgs& a, int z, int& L, int& btr,
+                                            size_t& qrow) {
+  if (a.prefill) {
+    const int r = z / a.max_chunk, i = z - r * a.max_chunk;
+    const int c0 = a.cu_q[r], c1 = a.cu_q[r + 1];
+    if (i >= c1 - c0) return false;
+    L = a.ctx_before[r] + i + 1;
+    btr = r;
+    qrow = (size_t)c0 + i;
+  } else {
+    L = a.context_lens[z];
+    btr = z;
+    qrow = (size_t)z;
+  }
+  return true;
+}
+
+template <int KVT, int D, int GMAX>
+__global__ __launch_bounds__(256) void decode_partial_vec(AttnArgs a) {
+  using S = VecShape<KVT, D>;
+  using QT = typename std::conditional<KVT == KV_F32, float, uint16_t>::type;
+  constexpr int EPL = S::EPL, R = S::R, RW = S::RW, U = S::U, TOK = S::TOK;
+
+  const int split = blockIdx.x, j = blockIdx.y, z = blockIdx.z;
+  int L, btr;
+  size_t qrow;
+  if (!resolve_row(a, z, L, btr, qrow)) return;
+  const int Hq = a.num_q_heads, Hkv = a.c.num_kv_heads, P = a.c.page_size;
+  const int G = Hq / Hkv;
+  const int t_begin = split * a.split_tokens;
+  if (t_begin >= L) {
+    if (split == 0) {  // empty context: output 0, lse = -inf
+      for (int i = threadIdx.x; i < G * D; i += blockDim.x)
+        store_o<QT>(a.out, (qrow * Hq + (size_t)j * G) * D + i, 0.0f);
+      if (a.lse && threadIdx.x < G) a.lse[qrow * Hq + (size_t)j * G + threadIdx.x] = -INFINITY;
+    }
+    return;
+  }
+  const int t_end = min(L, t_begin + a.split_tokens);
+  const int n_split = (L + a.split_tokens - 1) / a.split_tokens;
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int rg = lane / R, col = lane % R;
+
+  float kscale = 1.0f, vscale = 1.0f;
+  if constexpr (KVT == KV_FP8) { kscale = a.c.k_scale[j]; vscale = a.c.v_scale[j]; }
+  const float qmul = a.sm_scale * kLog2e * kscale;
+
+  float qf[GMAX][EPL];
+#pragma unroll
+  for (int g = 0; g < GMAX; ++g) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e)
+      qf[g][e] = (g < G) ? load_q<QT>(a.q, (qrow * Hq + (size_t)j * G + g) * D + col * EPL + e) * qmul
+                         : 0.0f;
+  }
+
+  float m[GMAX], l[GMAX], acc[GMAX][EPL];
+#pragma unroll
+  for (int g = 0; g < GMAX; ++g) {
+    m[g] = -INFINITY;
+    l[g] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[g][e] = 0.0f;
+  }
+
+  const int32_t* btrow = a.bt + (size_t)btr * a.bt_stride;
+  const uint8_t* kp = static_cast<const uint8_t*>(a.c.k_pool);
+  const uint8_t* vp = static_cast<const uint8_t*>(a.c.v_pool);
+  constexpr int ROWB = D * S::KVB;
+
+  for (int t0 = t_begin + w * TOK; t0 < t_end; t0 += kWaves * TOK) {
+    const int page = btrow[t0 / P];
+    const size_t base = (((size_t)page * Hkv + j) * P + (t0 % P)) * ROWB + (size_t)col * 16;
+    u32x4 kr[U], vr[U];
+    bool valid[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int rr = u * RW + rg;
+      valid[u] = (t0 + rr) < t_end;
+      const size_t off = base + (size_t)rr * ROWB;
+      kr[u] = valid[u] ? ld16(kp + off) : u32x4{0, 0, 0, 0};
+      vr[u] = valid[u] ? ld16(vp + off) : u32x4{0, 0, 0, 0};
+    }
+    float sc[GMAX][U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float kf[EPL];
+      piece_to_f32<KVT>(kr[u], kf);
+#pragma unroll
+      for (int g = 0; g < GMAX; ++g) {
+        float s = 0.0f;
+        if (g < G) {
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) s = fmaf(qf[g][e], kf[e], s);
+        }
+        s = group_sum<R>(s);
+        sc[g][u] = valid[u] ? s : -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < GMAX; ++g) {
+      if (g >= G) continue;
+      float mx = sc[g][0];
+#pragma unroll
+      for (int u = 1; u < U; ++u) mx = fmaxf(mx, sc[g][u]);
+      const float mn = fmaxf(m[g], mx);
+      if (mn == -INFINITY) continue;            // no valid row for this lane yet
+      const float alpha = __builtin_amdgcn_exp2f(m[g] - mn);   // exp2(-inf) = 0
+      l[g] *= alpha;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[g][e] *= alpha;
+      m[g] = mn;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float p = __builtin_amdgcn_exp2f(sc[g][u] - mn);
+        l[g] += p;
+        float vf[EPL];
+        piece_to_f32<KVT>(vr[u], vf);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(p, vf[e], acc[g][e]);
+      }
+    }
+  }
+
+  // Merge the row-groups of this wave (lanes that share `col`).
+#pragma unroll
+  for (int mask = R; mask < 64; mask <<= 1) {
+#pragma unroll
+    for (int g = 0; g < GMAX; ++g) {
+      if (g >= G) continue;
+      const float mo = __shfl_xor(m[g], mask, 64);
+      const float lo = __shfl_xor(l[g], mask, 64);
+      const float mn = fmaxf(m[g], mo);
+      const float fa = (m[g] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m[g] - mn);
+      const float fb = (mo == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mo - mn);
+      l[g] = l[g] * fa + lo * fb;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const float ao = __shfl_xor(acc[g][e], mask, 64);
+        acc[g][e] = acc[g][e] * fa + ao * fb;
+      }
+      m[g] = mn;
+    }
+  }
+
+  // Merge the waves through LDS.
+  __shared__ float sm_acc[kWaves][GMAX][D];
+  __shared__ float sm_m[kWaves][GMAX], sm_l[kWaves][GMAX];
+  if (rg == 0) {
+#pragma unroll
+    for (int g = 0; g < GMAX; ++g) {
+      if (g >= G) continue;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) sm_acc[w][g][col * EPL + e] = acc[g][e];
+      if (col == 0) { sm_m[w][g] = m[g]; sm_l[w][g] = l[g]; }
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
+    const int g = i / D, d = i - g * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, sm_m[ww][g]);
+    float lt = 0.0f, at = 0.0f;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) {
+      const float mw = sm_m[ww][g];
+      const float f = (mw == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
+      lt = fmaf(sm_l[ww][g], f, lt);
+      at = fmaf(sm_acc[ww][g][d], f, at);
+    }
+    const int h = j * G + g;
+    if (n_split == 1) {
+      store_o<QT>(a.out, (qrow * Hq + h) * D + d, at * vscale / lt);
+      if (d == 0 && a.lse) a.lse[qrow * Hq + h] = (M + __log2f(lt)) * kLn2;
+    } else {
+      const size_t slot = ((size_t)z * Hq + h) * a.max_splits + split;
+      a.ws_acc[slot * D + d] = at * vscale;
+      if (d == 0) { a.ws_ml[slot * 2] = M; a.ws_ml[slot * 2 + 1] = lt; }
+    }
+  }
+}
+
+// Merge: one wave per (row, query head); lanes cover head_dim.
+template <typename OT, int D>
+__global__ __launch_bounds__(256) void lse_merge_kernel(AttnArgs a) {
+  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int Hq = a.num_q_heads;
+  if (wid >= a.num_rows * Hq) return;
+  const int z = wid / Hq, h = wid - z * Hq;
+  const int L = a.context_lens[z];
+  const int n = (L + a.split_tokens - 1) / a.split_tokens;
+  if (n <= 1) return;
+  const size_t base = ((size_t)z * Hq + h) * a.max_splits;
+  float M = -INFINITY;
+  for (int s = 0; s < n; ++s) M = fmaxf(M, a.ws_ml[(base + s) * 2]);
+  float den = 0.0f;
+  constexpr int PER = D / 64;
+  float o[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) o[k] = 0.0f;
+  for (int s = 0; s < n; ++s) {
+    const float f = __builtin_amdgcn_exp2f(a.ws_ml[(base + s) * 2] - M);
+    den = fmaf(a.ws_ml[(base + s) * 2 + 1], f, den);
+#pragma unroll
+    for (int k = 0; k < PER; ++k) o[k] = fmaf(a.ws_acc[(base + s) * D + lane + 64 * k], f, o[k]);
+  }
+  const float inv = 1.0f / den;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) store_o<OT>(a.out, ((size_t)z * Hq + h) * D + lane + 64 * k, o[k] * inv);
+  if (lane == 0 && a.lse) a.lse[(size_t)z * Hq + h] = (M + __log2f(den)) * kLn2;
+}
+
+template <int KVT, int D>
+hipError_t launch_vec_d(const AttnArgs& a, dim3 grid, hipStream_t s) {
+  const int G = a.num_q_heads / a.c.num_kv_heads;
+  const dim3 block(256);
+  if (G <= 1) hipLaunchKernelGGL((decode_partial_vec<KVT, D, 1>), grid, block, 0, s, a);
+  else if (G <= 2) hipLaunchKernelGGL((decode_partial_vec<KVT, D, 2>), grid, block, 0, s, a);
+  else if (G <= 4) hipLaunchKernelGGL((decode_partial_vec<KVT, D, 4>), grid, block, 0, s, a);
+  else if (G <= 8) hipLaunchKernelGGL((decode_partial_vec<KVT, D, 8>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((decode_partial_vec<KVT, D, 16>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+template <int KVT>
+hipError_t launch_vec(const AttnArgs& a, dim3 grid, hipStream_t s) {
+  return a.c.head_dim == 64 ? launch_vec_d<KVT, 64>(a, grid, s) : launch_vec_d<KVT, 128>(a, grid, s);
+}
+
+hipError_t launch_vec_any(const AttnArgs& a, dim3 grid, hipStream_t s) {
+  switch (a.c.kv_dtype) {
+    case KV_F32: return launch_vec<KV_F32>(a, grid, s);
+    case KV_BF16: return launch_vec<KV_BF16>(a, grid, s);
+    default: return launch_vec<KV_FP8>(a, grid, s);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_partial(const AttnArgs& a, hipStream_t s) {
+  if (a.num_rows == 0) return hipSuccess;
+  const dim3 grid(a.max_splits, a.c.num_kv_heads, a.num_rows);
+  return launch_vec_any(a, grid, s);
+}
+
+hipError_t launch_lse_merge(const AttnArgs& a, hipStream_t s) {
+  if (a.num_rows == 0 || a.max_splits <= 1) return hipSuccess;
+  const int waves = a.num_rows * a.num_q_heads;
+  const dim3 grid((waves + 3) / 4), block(256);
+  const bool f32 = a.c.kv_dtype == KV_F32;
+  if (a.c.head_dim == 64) {
+    if (f32) hipLaunchKernelGGL((lse_merge_kernel<float, 64>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((lse_merge_kernel<uint16_t, 64>), grid, block, 0, s, a);
+  } else {
+    if (f32) hipLaunchKernelGGL((lse_merge_kernel<float, 128>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((lse_merge_kernel<uint16_t, 128>), grid, block, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+// Chunked prefill, generic path: every chunk row is a decode query over its
+// causal prefix (keys 0 .. ctx_before + i), one context range per row.
+hipError_t launch_prefill(const AttnArgs& a, hipStream_t s) {
+  if (a.num_rows == 0 || a.max_chunk == 0) return hipSuccess;
+  const dim3 grid(1, a.c.num_kv_heads, a.num_rows * a.max_chunk);
+  return launch_vec_any(a, grid, s);
+}
+
+}  // namespace pkv

@@ -1,0 +1,60 @@
+// Internal launch interface between the C ABI front end (api.cpp) and the
+// HIP kernels.  Host-side checks are done before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+struct CacheView {
+  const void* k_pool;
+  const void* v_pool;
+  void* k_pool_w;
+  void* v_pool_w;
+  const float* k_scale;
+  const float* v_scale;
+  int32_t num_pages, num_kv_heads, page_size, head_dim, kv_dtype;
+};
+
+struct AppendArgs {
+  CacheView c;
+  const void* k_new;
+  const void* v_new;
+  int32_t in_dtype;
+  const int32_t* cu;
+  const int32_t* start_pos;
+  const int32_t* bt;
+  int32_t bt_stride, num_rows, num_tokens;
+};
+
+// Rows of an attention launch are either decode sequences (one query each)
+// or prefill chunk rows (query i of request r).
+struct AttnArgs {
+  CacheView c;
+  const void* q;
+  void* out;
+  float* lse;
+  const int32_t* bt;
+  int32_t bt_stride;
+  const int32_t* context_lens;   // decode
+  const int32_t* cu_q;           // prefill
+  const int32_t* ctx_before;     // prefill
+  int32_t num_rows;              // decode: sequences; prefill: requests
+  int32_t max_chunk;             // prefill: longest chunk
+  int32_t num_q_heads;
+  int32_t split_tokens;
+  int32_t max_splits;
+  float sm_scale;
+  float* ws_acc;                 // [rows][Hq][max_splits][D]
+  float* ws_ml;                  // [rows][Hq][max_splits][2]
+  int32_t prefill;
+};
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t s);
+hipError_t launch_decode_partial(const AttnArgs& a, hipStream_t s);
+hipError_t launch_lse_merge(const AttnArgs& a, hipStream_t s);
+hipError_t launch_prefill(const AttnArgs& a, hipStream_t s);
+hipError_t launch_fp8_to_f32(const uint8_t* codes, float* out, int64_t n, hipStream_t s);
+
+}  // namespace pkv

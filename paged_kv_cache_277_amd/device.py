@@ -1,0 +1,165 @@
+"""Device-side plumbing for a generated workload: upload arrays with PyTorch,
+build the paged cache, and run the hot path through the C ABI.
+
+``DeviceWorkload.setup()`` fills the cache before the step (prompt tokens
+already cached); ``DeviceWorkload.step()`` is one pass of the hot path:
+append the step's new tokens, decode attention for every decode sequence
+(partial pass, then the log-sum-exp merge) and, for a mixed step, chunked
+prefill.  All of it runs in the library's kernels on one stream.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import binding as B
+from .workloads import POISON, Workload
+
+_TORCH_STORAGE = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}
+
+
+def _dev(x: np.ndarray, dtype: str, device) -> torch.Tensor:
+    """numpy array (float32 / uint16 bf16 bits / uint8 / int32) -> device tensor."""
+    x = np.ascontiguousarray(x)
+    if dtype == "bf16":
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(device)
+    if dtype == "f32":
+        return torch.from_numpy(x.astype(np.float32, copy=False)).to(device)
+    if dtype == "fp8":
+        return torch.from_numpy(x.astype(np.uint8, copy=False)).to(device)
+    if dtype == "i32":
+        return torch.from_numpy(x.astype(np.int32, copy=False)).to(device)
+    raise ValueError(dtype)
+
+
+def poisoned_pool(num_pages: int, Hkv: int, P: int, D: int, kv_dtype: str, device) -> torch.Tensor:
+    shape = (num_pages, Hkv, P, D)
+    if kv_dtype == "f32":
+        return torch.full(shape, int(POISON["f32"].view(np.int32)), dtype=torch.int32,
+                          device=device).view(torch.float32)
+    if kv_dtype == "bf16":
+        return torch.full(shape, int(POISON["bf16"].view(np.int16)), dtype=torch.int16,
+                          device=device).view(torch.bfloat16)
+    return torch.full(shape, int(POISON["fp8"]), dtype=torch.uint8, device=device)
+
+
+@dataclass
+class DeviceBatch:
+    k: torch.Tensor
+    v: torch.Tensor
+    cu: torch.Tensor
+    start: torch.Tensor
+    bt: torch.Tensor
+    rows: int
+    tokens: int
+
+
+@dataclass
+class DeviceWorkload:
+    wl: Workload
+    cache: B.PagedCache
+    setup_batch: DeviceBatch
+    step_batch: DeviceBatch
+    q: torch.Tensor
+    out: torch.Tensor
+    lse: torch.Tensor
+    bt: torch.Tensor
+    lens: torch.Tensor
+    max_len: int
+    split_tokens: int
+    workspace: Optional[torch.Tensor]
+    pf: dict = field(default_factory=dict)
+
+    def setup(self, stream=None) -> None:
+        self._append(self.setup_batch, stream)
+
+    def _append(self, b: DeviceBatch, stream=None) -> None:
+        if b.rows == 0:
+            return
+        B.pkv_kv_cache_append(self.cache, b.k, b.v, b.cu, b.start, b.bt, stream=stream)
+
+    def append_step(self, stream=None) -> None:
+        self._append(self.step_batch, stream)
+
+    def decode(self, stream=None) -> None:
+        if self.wl.num_seqs == 0:
+            return
+        B.pkv_paged_attn_decode(self.cache, self.q, self.out, self.bt, self.lens, self.max_len,
+                                float(self.wl.sm_scale), lse=self.lse,
+                                split_tokens=self.split_tokens, workspace=self.workspace,
+                                stream=stream)
+
+    def decode_partial(self, stream=None) -> None:
+        B.pkv_paged_attn_decode_partial(self.cache, self.q, self.out, self.bt, self.lens,
+                                        self.max_len, float(self.wl.sm_scale), lse=self.lse,
+                                        split_tokens=self.split_tokens, workspace=self.workspace,
+                                        stream=stream)
+
+    def merge(self, stream=None) -> None:
+        B.pkv_lse_merge(self.cache, self.out, self.lens, self.max_len, lse=self.lse,
+                        split_tokens=self.split_tokens, workspace=self.workspace, stream=stream)
+
+    def prefill(self, stream=None) -> None:
+        if not self.pf:
+            return
+        p = self.pf
+        B.pkv_paged_attn_chunked_prefill(self.cache, p["q"], p["out"], p["cu"], p["ctx"], p["bt"],
+                                         p["max_chunk"], float(self.wl.sm_scale), lse=p["lse"],
+                                         stream=stream)
+
+    def step(self, stream=None) -> None:
+        """One pass of the hot path: append -> decode (partial + merge) -> prefill."""
+        self.append_step(stream)
+        self.decode(stream)
+        self.prefill(stream)
+
+
+def upload(wl: Workload, device="cuda", split_tokens: int = 0) -> DeviceWorkload:
+    s = wl.spec
+    kp = poisoned_pool(wl.num_pages, s.num_kv_heads, s.page_size, s.head_dim, s.kv_dtype, device)
+    vp = poisoned_pool(wl.num_pages, s.num_kv_heads, s.page_size, s.head_dim, s.kv_dtype, device)
+    ks = vs = None
+    if s.kv_dtype == "fp8":
+        ks = torch.from_numpy(wl.k_scale).to(device)
+        vs = torch.from_numpy(wl.v_scale).to(device)
+    cache = B.PagedCache(kp, vp, ks, vs)
+
+    def batch(b) -> DeviceBatch:
+        return DeviceBatch(k=_dev(b.k, s.kv_in_dtype, device), v=_dev(b.v, s.kv_in_dtype, device),
+                           cu=_dev(b.cu, "i32", device), start=_dev(b.start_pos, "i32", device),
+                           bt=_dev(b.block_tables, "i32", device), rows=b.num_rows,
+                           tokens=b.num_tokens)
+
+    q = _dev(wl.q, s.q_dtype, device)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=device)
+    max_len = int(wl.context_lens.max()) if wl.num_seqs else 0
+    split = split_tokens or (B.pkv_decode_split_tokens(cache, wl.num_seqs, s.num_q_heads, max_len)
+                             if wl.num_seqs else 0)
+    ws = (B.decode_workspace(cache, wl.num_seqs, s.num_q_heads, max_len, split)
+          if wl.num_seqs else None)
+    dw = DeviceWorkload(wl=wl, cache=cache, setup_batch=batch(wl.setup), step_batch=batch(wl.step),
+                        q=q, out=out, lse=lse, bt=_dev(wl.block_tables, "i32", device),
+                        lens=_dev(wl.context_lens, "i32", device), max_len=max_len,
+                        split_tokens=split, workspace=ws)
+    if wl.num_prefill:
+        pq = _dev(wl.pf_q, s.q_dtype, device)
+        dw.pf = dict(q=pq, out=torch.empty_like(pq),
+                     lse=torch.empty(pq.shape[:2], dtype=torch.float32, device=device),
+                     cu=_dev(wl.pf_cu, "i32", device), ctx=_dev(wl.pf_ctx_before, "i32", device),
+                     bt=_dev(wl.pf_block_tables, "i32", device),
+                     max_chunk=int(np.diff(wl.pf_cu).max()))
+    return dw
+
+
+def storage_to_numpy(t: torch.Tensor) -> np.ndarray:
+    """Device tensor -> numpy in the storage representation the oracle uses."""
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).numpy()
+    return t.numpy()
