@@ -72,6 +72,28 @@ def cpu_baseline(wl, budget_s: float = 12.0) -> dict:
                       f"fp64 numpy"}
 
 
+def copy_calibration(args) -> int:
+    """A plain device-to-device copy of 1 GiB (torch's copy kernel): the known
+    read and write volume against which HBM byte counters are scaled."""
+    import torch
+    n = 1 << 30
+    a = torch.ones(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(args.warmup):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(args.steps):
+        b.copy_(a)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / args.steps
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms_per_copy": round(ms, 5),
+                      "copy_GBps_read_plus_write": round(2 * n / ms / 1e6, 1)}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -81,6 +103,8 @@ def main() -> int:
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="time a plain device copy of known size instead (counter scaling)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -95,6 +119,8 @@ def main() -> int:
     from paged_kv_cache_277_amd import workloads as wk
 
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        return copy_calibration(args)
     spec = wk.CONFIGS[args.workload]
     t0 = time.perf_counter()
     wl = wk.make_workload(spec)

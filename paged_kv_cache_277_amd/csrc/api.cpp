@@ -102,8 +102,9 @@ int32_t default_split(const pkv_cache_desc* c, int32_t num_seqs, int32_t max_len
   int split = c->kv_dtype == PKV_FP8_E4M3FN ? 1024 : 512;
   if (c->head_dim == 64) split *= 2;
   split = std::max(gran, split / gran * gran);
+  const int floor_split = std::max(gran, 256);   // below this the merge costs more than it hides
   const int64_t pairs = (int64_t)std::max(1, num_seqs) * c->num_kv_heads;
-  while (split > 2 * gran && pairs * ceil_div(std::max(1, max_len), split) < 8 * kNumCUs)
+  while (split / 2 >= floor_split && pairs * ceil_div(std::max(1, max_len), split) < 8 * kNumCUs)
     split = std::max(gran, split / 2 / gran * gran);
   if (max_len <= split) split = std::max(gran, ceil_div(std::max(1, max_len), gran) * gran);
   return split;
@@ -168,6 +169,8 @@ pkv_status prepare_decode(const pkv_cache_desc* cache, const void* q, int32_t q_
     return fail(PKV_ERR_INVALID_ARG, "workspace of %zu bytes needed, %zu given", need,
                 workspace_bytes_in);
   const int32_t ms = std::max(1, ceil_div(std::max(0, max_context_len), split));
+  if (ms > kMaxGridYZ)
+    return fail(PKV_ERR_UNSUPPORTED, "%d context ranges per sequence (max %d)", ms, kMaxGridYZ);
   std::memset(a, 0, sizeof *a);
   a->c = view(cache);
   a->q = q;
@@ -181,6 +184,7 @@ pkv_status prepare_decode(const pkv_cache_desc* cache, const void* q, int32_t q_
   a->split_tokens = split;
   a->max_splits = ms;
   a->sm_scale = sm_scale;
+  a->page_shift = __builtin_ctz((unsigned)cache->page_size);
   if (need > 0) {
     char* w = static_cast<char*>(const_cast<void*>(workspace));
     const size_t n = (size_t)num_seqs * num_q_heads * ms;
@@ -338,6 +342,7 @@ pkv_status pkv_paged_attn_chunked_prefill(const pkv_cache_desc* cache, const voi
   a.max_splits = 1;
   a.sm_scale = sm_scale;
   a.prefill = 1;
+  a.page_shift = __builtin_ctz((unsigned)cache->page_size);
   return hip_status(pkv::launch_prefill(a, static_cast<hipStream_t>(stream)),
                     "paged_attn_chunked_prefill");
 }

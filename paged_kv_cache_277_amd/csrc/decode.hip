@@ -25,6 +25,8 @@
 // m is kept in the log2 domain (scores are pre-multiplied by log2(e)).
 #include <math.h>
 
+#include <type_traits>
+
 #include "pkv_device.h"
 #include "pkv_launch.h"
 
@@ -94,17 +96,46 @@ __device__ __forceinline__ bool resolve_row(const AttnArgs& a, int z, int& L, in
   return true;
 }
 
+// Load EPL query elements of one head at `idx` (16-byte loads), scaled.
+template <typename QT, int EPL>
+__device__ __forceinline__ void load_q_slice(const void* q, size_t idx, float mul, float* out) {
+  if constexpr (sizeof(QT) == 4) {
+    static_assert(EPL % 4 == 0, "");
+#pragma unroll
+    for (int c = 0; c < EPL / 4; ++c) {
+      const u32x4 x = ld16(static_cast<const float*>(q) + idx + 4 * c);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) out[4 * c + i] = __uint_as_float(x[i]) * mul;
+    }
+  } else {
+    static_assert(EPL % 8 == 0, "");
+#pragma unroll
+    for (int c = 0; c < EPL / 8; ++c) {
+      const u32x4 x = ld16(static_cast<const uint16_t*>(q) + idx + 8 * c);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        out[8 * c + 2 * i] = bf16_lo(x[i]) * mul;
+        out[8 * c + 2 * i + 1] = bf16_hi(x[i]) * mul;
+      }
+    }
+  }
+}
+
 template <int KVT, int D, int GMAX>
 __global__ __launch_bounds__(256) void decode_partial_vec(AttnArgs a) {
   using S = VecShape<KVT, D>;
   using QT = typename std::conditional<KVT == KV_F32, float, uint16_t>::type;
   constexpr int EPL = S::EPL, R = S::R, RW = S::RW, U = S::U, TOK = S::TOK;
+  constexpr int ROWB = D * S::KVB;                 // bytes of one token row of one head
 
-  const int split = blockIdx.x, j = blockIdx.y, z = blockIdx.z;
+  // KV heads are the fastest grid dimension: workgroups dispatched together
+  // read the head slabs of the same physical pages, which sit side by side.
+  const int j = blockIdx.x, split = blockIdx.y, z = blockIdx.z;
   int L, btr;
   size_t qrow;
   if (!resolve_row(a, z, L, btr, qrow)) return;
-  const int Hq = a.num_q_heads, Hkv = a.c.num_kv_heads, P = a.c.page_size;
+  const int Hq = a.num_q_heads, Hkv = a.c.num_kv_heads;
+  const int pshift = a.page_shift, pmask = (1 << pshift) - 1;
   const int G = Hq / Hkv;
   const int t_begin = split * a.split_tokens;
   if (t_begin >= L) {
@@ -118,7 +149,8 @@ __global__ __launch_bounds__(256) void decode_partial_vec(AttnArgs a) {
   const int t_end = min(L, t_begin + a.split_tokens);
   const int n_split = (L + a.split_tokens - 1) / a.split_tokens;
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = uniform(threadIdx.x >> 6);
   const int rg = lane / R, col = lane % R;
 
   float kscale = 1.0f, vscale = 1.0f;
@@ -128,10 +160,12 @@ __global__ __launch_bounds__(256) void decode_partial_vec(AttnArgs a) {
   float qf[GMAX][EPL];
 #pragma unroll
   for (int g = 0; g < GMAX; ++g) {
+    if (g < G) {
+      load_q_slice<QT, EPL>(a.q, (qrow * Hq + (size_t)j * G + g) * D + col * EPL, qmul, qf[g]);
+    } else {
 #pragma unroll
-    for (int e = 0; e < EPL; ++e)
-      qf[g][e] = (g < G) ? load_q<QT>(a.q, (qrow * Hq + (size_t)j * G + g) * D + col * EPL + e) * qmul
-                         : 0.0f;
+      for (int e = 0; e < EPL; ++e) qf[g][e] = 0.0f;
+    }
   }
 
   float m[GMAX], l[GMAX], acc[GMAX][EPL];
@@ -146,26 +180,46 @@ __global__ __launch_bounds__(256) void decode_partial_vec(AttnArgs a) {
   const int32_t* btrow = a.bt + (size_t)btr * a.bt_stride;
   const uint8_t* kp = static_cast<const uint8_t*>(a.c.k_pool);
   const uint8_t* vp = static_cast<const uint8_t*>(a.c.v_pool);
-  constexpr int ROWB = D * S::KVB;
+  // Byte offset of this lane's piece inside a 16-token tile of page `page`.
+  const size_t lane_off = (size_t)rg * ROWB + (size_t)col * 16;
+  auto tile_base = [&](int page, int t) -> size_t {
+    return (((size_t)page * Hkv + j) << pshift | (size_t)(t & pmask)) * ROWB + lane_off;
+  };
+  constexpr int STRIDE = kWaves * TOK;
 
-  for (int t0 = t_begin + w * TOK; t0 < t_end; t0 += kWaves * TOK) {
-    const int page = btrow[t0 / P];
-    const size_t base = (((size_t)page * Hkv + j) * P + (t0 % P)) * ROWB + (size_t)col * 16;
-    u32x4 kr[U], vr[U];
-    bool valid[U];
+  // Software pipeline: the next tile's K/V loads are in flight while the
+  // current tile is scored; block-table entries are read one tile ahead.
+  int t0 = t_begin + w * TOK;
+  u32x4 kA[U], vA[U];
+  int page_next = 0;
+  if (t0 < t_end) {
+    const size_t base = tile_base(btrow[t0 >> pshift], t0);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int rr = u * RW + rg;
-      valid[u] = (t0 + rr) < t_end;
-      const size_t off = base + (size_t)rr * ROWB;
-      kr[u] = valid[u] ? ld16(kp + off) : u32x4{0, 0, 0, 0};
-      vr[u] = valid[u] ? ld16(vp + off) : u32x4{0, 0, 0, 0};
+      kA[u] = ld16(kp + base + (size_t)u * RW * ROWB);
+      vA[u] = ld16(vp + base + (size_t)u * RW * ROWB);
     }
+    if (t0 + STRIDE < t_end) page_next = btrow[(t0 + STRIDE) >> pshift];
+  }
+  for (; t0 < t_end; t0 += STRIDE) {
+    const int t1 = t0 + STRIDE;
+    u32x4 kB[U], vB[U];
+    if (t1 < t_end) {
+      const size_t base = tile_base(page_next, t1);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        kB[u] = ld16(kp + base + (size_t)u * RW * ROWB);
+        vB[u] = ld16(vp + base + (size_t)u * RW * ROWB);
+      }
+      if (t1 + STRIDE < t_end) page_next = btrow[(t1 + STRIDE) >> pshift];
+    }
+    const bool full = t0 + TOK <= t_end;
     float sc[GMAX][U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      const bool valid = full || (t0 + u * RW + rg < t_end);
       float kf[EPL];
-      piece_to_f32<KVT>(kr[u], kf);
+      piece_to_f32<KVT>(kA[u], kf);
 #pragma unroll
       for (int g = 0; g < GMAX; ++g) {
         float s = 0.0f;
@@ -174,32 +228,44 @@ __global__ __launch_bounds__(256) void decode_partial_vec(AttnArgs a) {
           for (int e = 0; e < EPL; ++e) s = fmaf(qf[g][e], kf[e], s);
         }
         s = group_sum<R>(s);
-        sc[g][u] = valid[u] ? s : -INFINITY;
+        sc[g][u] = valid ? s : -INFINITY;
       }
+      if (!valid) vA[u] = u32x4{0, 0, 0, 0};   // unused slots may hold NaN
     }
+    float p[GMAX][U];
 #pragma unroll
     for (int g = 0; g < GMAX; ++g) {
-      if (g >= G) continue;
       float mx = sc[g][0];
 #pragma unroll
       for (int u = 1; u < U; ++u) mx = fmaxf(mx, sc[g][u]);
       const float mn = fmaxf(m[g], mx);
-      if (mn == -INFINITY) continue;            // no valid row for this lane yet
-      const float alpha = __builtin_amdgcn_exp2f(m[g] - mn);   // exp2(-inf) = 0
+      // mn is finite for every lane with a valid row so far; lanes with none
+      // keep m = -inf and p = 0 (exp2 of -inf is 0, and -inf - -inf is avoided).
+      const float alpha = (mn == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m[g] - mn);
       l[g] *= alpha;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[g][e] *= alpha;
       m[g] = mn;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const float p = __builtin_amdgcn_exp2f(sc[g][u] - mn);
-        l[g] += p;
-        float vf[EPL];
-        piece_to_f32<KVT>(vr[u], vf);
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(p, vf[e], acc[g][e]);
+        p[g][u] = (mn == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sc[g][u] - mn);
+        l[g] += p[g][u];
       }
     }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float vf[EPL];
+      piece_to_f32<KVT>(vA[u], vf);
+#pragma unroll
+      for (int g = 0; g < GMAX; ++g) {
+        if (g < G) {
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(p[g][u], vf[e], acc[g][e]);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) { kA[u] = kB[u]; vA[u] = vB[u]; }
   }
 
   // Merge the row-groups of this wave (lanes that share `col`).
@@ -321,7 +387,7 @@ hipError_t launch_vec_any(const AttnArgs& a, dim3 grid, hipStream_t s) {
 
 hipError_t launch_decode_partial(const AttnArgs& a, hipStream_t s) {
   if (a.num_rows == 0) return hipSuccess;
-  const dim3 grid(a.max_splits, a.c.num_kv_heads, a.num_rows);
+  const dim3 grid(a.c.num_kv_heads, a.max_splits, a.num_rows);
   return launch_vec_any(a, grid, s);
 }
 
@@ -344,7 +410,7 @@ hipError_t launch_lse_merge(const AttnArgs& a, hipStream_t s) {
 // causal prefix (keys 0 .. ctx_before + i), one context range per row.
 hipError_t launch_prefill(const AttnArgs& a, hipStream_t s) {
   if (a.num_rows == 0 || a.max_chunk == 0) return hipSuccess;
-  const dim3 grid(1, a.c.num_kv_heads, a.num_rows * a.max_chunk);
+  const dim3 grid(a.c.num_kv_heads, 1, a.num_rows * a.max_chunk);
   return launch_vec_any(a, grid, s);
 }
 

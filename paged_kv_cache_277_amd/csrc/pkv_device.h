@@ -83,12 +83,35 @@ __device__ __forceinline__ u32x4 ld16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
-// Sum / max over aligned groups of N lanes (N a power of two <= 64).
+// DPP lane moves within a row of 16 lanes (gfx9 DPP controls).
+enum : int {
+  DPP_XOR1 = 0xB1,        // quad_perm [1,0,3,2]
+  DPP_XOR2 = 0x4E,        // quad_perm [2,3,0,1]
+  DPP_HALF_MIRROR = 0x141,  // lane i <-> 7-i inside each half row
+  DPP_MIRROR = 0x140,       // lane i <-> 15-i inside each row
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of N consecutive lanes (N a power of two <= 64);
+// every lane of a group receives the group's sum.  Inside a 16-lane row the
+// steps are DPP moves folded into the adds; wider groups cross rows with a
+// lane shuffle.
 template <int N>
 __device__ __forceinline__ float group_sum(float x) {
-#pragma unroll
-  for (int m = 1; m < N; m <<= 1) x += __shfl_xor(x, m, 64);
+  if constexpr (N >= 2) x += dpp_mov<DPP_XOR1>(x);
+  if constexpr (N >= 4) x += dpp_mov<DPP_XOR2>(x);
+  if constexpr (N >= 8) x += dpp_mov<DPP_HALF_MIRROR>(x);
+  if constexpr (N >= 16) x += dpp_mov<DPP_MIRROR>(x);
+  if constexpr (N >= 32) x += __shfl_xor(x, 16, 64);
+  if constexpr (N >= 64) x += __shfl_xor(x, 32, 64);
   return x;
 }
+
+// Wave-uniform copy of a value (lets the compiler keep it in an SGPR).
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 }  // namespace pkv

@@ -49,6 +49,7 @@ struct AttnArgs {
   float* ws_acc;                 // [rows][Hq][max_splits][D]
   float* ws_ml;                  // [rows][Hq][max_splits][2]
   int32_t prefill;
+  int32_t page_shift;            // log2(page_size)
 };
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
