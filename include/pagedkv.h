@@ -263,8 +263,9 @@ pkv_status pkv_validate_block_tables(const pkv_cache_desc* cache, const int32_t*
                                      int32_t bt_stride, const int32_t* lens, int32_t num_seqs,
                                      void* stream);
 
-/* Decode n fp8 e4m3fn codes (device uint8[n]) to float (device float[n]) with
- * the same device conversion the attention kernels use. */
+/* Decode n fp8 e4m3fn codes (device uint8[n], 4-byte aligned) to float
+ * (device float[n]) with the device conversion of the matrix-core attention
+ * path (fp8 -> bf16, exact). */
 pkv_status pkv_fp8_e4m3fn_to_f32(const uint8_t* codes, float* out, int64_t n, void* stream);
 
 #ifdef __cplusplus

@@ -69,20 +69,20 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   }
 }
 
+// Decodes through the fp8 -> bf16 conversion of the matrix-core attention
+// path (the bf16 result widens to float exactly).
 __global__ __launch_bounds__(256) void fp8_to_f32_kernel(const uint8_t* codes, float* out, int64_t n) {
   const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (i >= n) return;
+  uint32_t w = 0;
   if (i + 4 <= n) {
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(codes + i);
-    float o[4];
-    fp8x4_to_f32(w, o);
-    out[i] = o[0]; out[i + 1] = o[1]; out[i + 2] = o[2]; out[i + 3] = o[3];
-  } else if (i < n) {
-    uint32_t w = 0;
+    w = *reinterpret_cast<const uint32_t*>(codes + i);
+  } else {
     for (int64_t k = i; k < n; ++k) w |= uint32_t(codes[k]) << (8 * (k - i));
-    float o[4];
-    fp8x4_to_f32(w, o);
-    for (int64_t k = i; k < n; ++k) out[k] = o[k - i];
   }
+  const uint32_t lo = fp8x2_to_bf16x2<false>(w), hi = fp8x2_to_bf16x2<true>(w);
+  const float o[4] = {bf16_lo(lo), bf16_hi(lo), bf16_lo(hi), bf16_hi(hi)};
+  for (int k = 0; k < 4 && i + k < n; ++k) out[i + k] = o[k];
 }
 
 }  // namespace

@@ -387,6 +387,7 @@ hipError_t launch_vec_any(const AttnArgs& a, dim3 grid, hipStream_t s) {
 
 hipError_t launch_decode_partial(const AttnArgs& a, hipStream_t s) {
   if (a.num_rows == 0) return hipSuccess;
+  if (decode_mfma_supported(a)) return launch_decode_partial_mfma(a, s);
   const dim3 grid(a.c.num_kv_heads, a.max_splits, a.num_rows);
   return launch_vec_any(a, grid, s);
 }

@@ -1,0 +1,347 @@
+// Paged decode attention for grouped query heads on the matrix cores (MFMA).
+//
+// Same method as the vector path (block-table walk, running max / running
+// sum: "TensorRT-LLM框架解析与高性能推理优化实践" §6.1-§6.2; scaled dot-product
+// attention; per-head fp8 KV scales dequantised in the kernel, §7.2), for
+// query groups G = Hq/Hkv >= 3, where the G heads that share a KV head turn
+// decode into a small dense contraction per 32-token tile:
+//
+//   S^T[t][h] = sum_d K[t][d] Q[h][d]        v_mfma_f32_16x16x32_bf16, M = 16 tokens,
+//                                            N = 16 head slots (G used), K = 32 of d
+//   O^T[d][h] += sum_t V[t][d] P^T[t][h]     M = 16 of d, N = 16 head slots, K = 32 tokens
+//
+// Lane layouts of the 16x16x32 bf16 MFMA (wave64): A[i][k] in lane i%16 +
+// 16*(k/8), element k%8; B[k][j] in lane j + 16*(k/8); C[i][j] in lane
+// j + 16*(i/4), element i%4.  Consequences used below:
+//   * K rows go straight from HBM to the A operand: lane l reads 64
+//     contiguous bytes (bf16) or 32 (fp8) of token l%16 covering
+//     d in [32g, 32g+32), g = l/16; MFMA step kk uses d = 32g + 8kk + e.  The
+//     contraction over d is order-free, so Q^T (B operand) is loaded in the
+//     same d order.
+//   * The S^T result leaves, in lane l, head h = l%16 for tokens 4g+r of each
+//     16-token block; over the two blocks of a tile that is 8 tokens of one
+//     head — exactly a B operand row of P^T if the tile's tokens are taken in
+//     the order (4g..4g+3, 16+4g..16+4g+3).  No lane shuffle is needed.
+//   * O^T accumulates in lane l for head h = l%16, so the online-softmax
+//     rescale of a head touches only that lane's registers.
+//   * V^T (A operand of the second product) needs 8 tokens of one d per lane:
+//     the tile's V rows are written row-major to this wave's LDS slice with
+//     16-byte stores and read back with gfx950's transpose read
+//     (ds_read_b64_tr_b16: inside each 16-lane group, lane i receives element
+//     i%4 of the 4-element reads of lanes 4r + i/4, r = 0..3).  Two such reads
+//     give one A operand.
+//
+// Work decomposition: like the vector path, one workgroup of 4 waves per
+// (row, KV head, context range); each wave walks 32-token tiles of the range
+// with its own softmax state, the next tile's K/V loads in flight while the
+// current tile is computed.  Scores are kept in the log2 domain.
+#include <math.h>
+
+#include "pkv_device.h"
+#include "pkv_launch.h"
+
+namespace pkv {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kTile = 32;                      // tokens per wave tile
+
+typedef __bf16 bf16x8_t __attribute__((__vector_size__(16)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// 16 fp8 codes -> 16 bf16 (two u32x4).
+__device__ __forceinline__ void fp8x16_to_bf16(const u32x4& x, u32x4& lo, u32x4& hi) {
+  lo[0] = fp8x2_to_bf16x2<false>(x[0]); lo[1] = fp8x2_to_bf16x2<true>(x[0]);
+  lo[2] = fp8x2_to_bf16x2<false>(x[1]); lo[3] = fp8x2_to_bf16x2<true>(x[1]);
+  hi[0] = fp8x2_to_bf16x2<false>(x[2]); hi[1] = fp8x2_to_bf16x2<true>(x[2]);
+  hi[2] = fp8x2_to_bf16x2<false>(x[3]); hi[3] = fp8x2_to_bf16x2<true>(x[3]);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return uint32_t(f32_to_bf16_rne(a)) | (uint32_t(f32_to_bf16_rne(b)) << 16);
+}
+
+// Per-lane register image of one 32-token tile.
+//   K: for each 16-token block, the lane's 32 d-values of token l%16 as bf16
+//      (KB = 4 u32x4 per block for bf16 storage; fp8 is loaded as 2 u32x4 and
+//      widened when used).
+//   V: row-major pieces for the LDS image: lane l holds 16-byte piece l%R of
+//      rows (l/R) + (64/R)*i.
+template <int KVT, int D>
+struct TileRegs {
+  static constexpr int KVB = KvBytes<KVT>::value;
+  static constexpr int DPL = D / 4;                    // d values per lane group
+  static constexpr int KPL = (DPL * KVB) / 16;         // K 16-byte loads per lane per block
+  static constexpr int VROWB = D * KVB;                // bytes per V row in the pool
+  static constexpr int VLOADS = (kTile * VROWB) / (64 * 16);  // V 16-byte loads per lane
+  u32x4 k[2][KPL];
+  u32x4 v[VLOADS];
+};
+
+template <int KVT, int D, bool MASKED>
+__device__ __forceinline__ void load_tile(TileRegs<KVT, D>& r, const uint8_t* kp, const uint8_t* vp,
+                                          const int32_t* btrow, int t0, int t_end, int Hkv, int j,
+                                          int pshift, int lane) {
+  using TR = TileRegs<KVT, D>;
+  constexpr int ROWB = TR::VROWB;
+  const int pmask = (1 << pshift) - 1;
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    const int tb = t0 + 16 * blk;
+    // A block past the end reuses the first block's page (in bounds; masked later).
+    const int page = btrow[(MASKED && tb >= t_end ? t0 : tb) >> pshift];
+    const size_t row = (((size_t)page * Hkv + j) << pshift | (size_t)(tb & pmask));
+    // K: token (lane % 16), d-range [g*D/4, (g+1)*D/4)
+    const uint8_t* kbase = kp + (row + (lane & 15)) * ROWB + (size_t)(lane >> 4) * TR::DPL * TR::KVB;
+#pragma unroll
+    for (int i = 0; i < TR::KPL; ++i) r.k[blk][i] = ld16(kbase + 16 * i);
+    // V: rows of this block, 16-byte pieces in row-major order
+    constexpr int R = ROWB / 16;                 // lanes per row
+    constexpr int RPI = 64 / R;                  // rows per load instruction
+    constexpr int LPB = TR::VLOADS / 2;          // loads per lane per block
+#pragma unroll
+    for (int i = 0; i < LPB; ++i) {
+      const int rr = (lane / R) + RPI * i;       // row within the block (0..15)
+      r.v[blk * LPB + i] = ld16(vp + (row + rr) * ROWB + (size_t)(lane % R) * 16);
+    }
+  }
+}
+
+template <int KVT, int D>
+__global__ __launch_bounds__(256, 2) void decode_partial_mfma(AttnArgs a) {
+  using TR = TileRegs<KVT, D>;
+  constexpr int KK = D / 32;                    // MFMA steps over d
+  constexpr int DT = D / 16;                    // 16-wide d tiles of the output
+  constexpr int ROWB = TR::VROWB;
+  constexpr int R = ROWB / 16, RPI = 64 / R, LPB = TR::VLOADS / 2;
+  constexpr int LDS_ROW = D * 2;                // bf16 V rows in LDS
+  constexpr int STAGE_BYTES = kWaves * kTile * LDS_ROW;
+  constexpr int MERGE_BYTES = (kWaves * 16 * D + kWaves * 32) * 4;
+  __shared__ __attribute__((aligned(16)))
+  uint8_t smem[STAGE_BYTES > MERGE_BYTES ? STAGE_BYTES : MERGE_BYTES];
+
+  const int j = blockIdx.x, split = blockIdx.y, z = blockIdx.z;
+  const int L = a.context_lens[z];
+  const int Hq = a.num_q_heads, Hkv = a.c.num_kv_heads;
+  const int G = Hq / Hkv;
+  const int t_begin = split * a.split_tokens;
+  const size_t qrow = (size_t)z;
+  if (t_begin >= L) {
+    if (split == 0) {
+      for (int i = threadIdx.x; i < G * D; i += blockDim.x)
+        static_cast<uint16_t*>(a.out)[(qrow * Hq + (size_t)j * G) * D + i] = 0;
+      if (a.lse && threadIdx.x < G) a.lse[qrow * Hq + (size_t)j * G + threadIdx.x] = -INFINITY;
+    }
+    return;
+  }
+  const int t_end = min(L, t_begin + a.split_tokens);
+  const int n_split = (L + a.split_tokens - 1) / a.split_tokens;
+  const int lane = threadIdx.x & 63;
+  const int w = uniform(threadIdx.x >> 6);
+  const int g4 = lane >> 4, h = lane & 15;       // lane group and head slot
+  const int pshift = a.page_shift;
+
+  float kscale = 1.0f, vscale = 1.0f;
+  if constexpr (KVT == KV_FP8) { kscale = a.c.k_scale[j]; vscale = a.c.v_scale[j]; }
+  const float smul = a.sm_scale * kLog2e * kscale;
+
+  // Q^T as B operand: lane (g, h) holds Q[j*G + h][g*D/4 + 8kk + e]; zero for h >= G.
+  u32x4 qb[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) qb[kk] = u32x4{0, 0, 0, 0};
+  if (h < G) {
+    const uint16_t* q = static_cast<const uint16_t*>(a.q) + (qrow * Hq + (size_t)j * G + h) * D;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) qb[kk] = ld16(q + (D / 4) * g4 + 8 * kk);
+  }
+
+  f32x4 o[DT];
+#pragma unroll
+  for (int i = 0; i < DT; ++i) o[i] = f32x4{0, 0, 0, 0};
+  float m = -INFINITY, l = 0.0f;
+
+  const int32_t* btrow = a.bt + (size_t)z * a.bt_stride;
+  const uint8_t* kp = static_cast<const uint8_t*>(a.c.k_pool);
+  const uint8_t* vp = static_cast<const uint8_t*>(a.c.v_pool);
+  uint8_t* lds = smem + w * kTile * LDS_ROW;
+  constexpr int STRIDE = kWaves * kTile;
+
+  int t0 = t_begin + w * kTile;
+  TR cur, nxt;
+  if (t0 < t_end) {
+    if (t0 + kTile <= t_end) load_tile<KVT, D, false>(cur, kp, vp, btrow, t0, t_end, Hkv, j, pshift, lane);
+    else load_tile<KVT, D, true>(cur, kp, vp, btrow, t0, t_end, Hkv, j, pshift, lane);
+  }
+  for (; t0 < t_end; t0 += STRIDE) {
+    const int t1 = t0 + STRIDE;
+    if (t1 < t_end) {
+      if (t1 + kTile <= t_end) load_tile<KVT, D, false>(nxt, kp, vp, btrow, t1, t_end, Hkv, j, pshift, lane);
+      else load_tile<KVT, D, true>(nxt, kp, vp, btrow, t1, t_end, Hkv, j, pshift, lane);
+    }
+    const bool full = t0 + kTile <= t_end;
+
+    // ---- V rows -> LDS (row-major bf16), zeroing rows past the end ----
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+#pragma unroll
+      for (int i = 0; i < LPB; ++i) {
+        const int rr = (lane / R) + RPI * i;
+        const int tok = 16 * blk + rr;
+        u32x4 x = cur.v[blk * LPB + i];
+        if (!full && t0 + tok >= t_end) x = u32x4{0, 0, 0, 0};
+        if constexpr (KVT == KV_FP8) {
+          u32x4 lo, hi;
+          fp8x16_to_bf16(x, lo, hi);
+          uint8_t* dst = lds + tok * LDS_ROW + (lane % R) * 32;
+          *reinterpret_cast<u32x4*>(dst) = lo;
+          *reinterpret_cast<u32x4*>(dst + 16) = hi;
+        } else {
+          *reinterpret_cast<u32x4*>(lds + tok * LDS_ROW + (lane % R) * 16) = x;
+        }
+      }
+    }
+
+    // ---- S^T = K Q^T for the two 16-token blocks ----
+    f32x4 s[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      f32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        u32x4 ka;
+        if constexpr (KVT == KV_FP8) {
+          // fp8: the lane's 32 codes are two u32x4; step kk uses codes 8kk..8kk+7
+          const u32x4& src = cur.k[blk][kk >> 1];
+          const int o2 = (kk & 1) * 2;
+          ka[0] = fp8x2_to_bf16x2<false>(src[o2]);
+          ka[1] = fp8x2_to_bf16x2<true>(src[o2]);
+          ka[2] = fp8x2_to_bf16x2<false>(src[o2 + 1]);
+          ka[3] = fp8x2_to_bf16x2<true>(src[o2 + 1]);
+        } else {
+          ka = cur.k[blk][kk];
+        }
+        acc = mfma16(ka, qb[kk], acc);
+      }
+      s[blk] = acc;
+    }
+
+    // ---- online softmax for head h over the tile's 32 tokens ----
+    // lane (g, h) holds tokens 4g + r (block 0) and 16 + 4g + r (block 1)
+    float sv[8];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tok = 16 * blk + 4 * g4 + r;
+        const float x = s[blk][r] * smul;
+        sv[4 * blk + r] = (full || t0 + tok < t_end) ? x : -INFINITY;
+      }
+    float mx = sv[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mn = fmaxf(m, mx);               // finite: every tile has a valid token
+    const float alpha = __builtin_amdgcn_exp2f(m - mn);
+    m = mn;
+    float p[8];
+    float psum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) { p[i] = __builtin_amdgcn_exp2f(sv[i] - mn); psum += p[i]; }
+    l = l * alpha + psum;
+#pragma unroll
+    for (int i = 0; i < DT; ++i) o[i] *= alpha;
+    u32x4 pb;                                    // P^T as B operand (token order above)
+    pb[0] = pack_bf16x2(p[0], p[1]);
+    pb[1] = pack_bf16x2(p[2], p[3]);
+    pb[2] = pack_bf16x2(p[4], p[5]);
+    pb[3] = pack_bf16x2(p[6], p[7]);
+
+    // ---- O^T += V^T P^T, V^T from the LDS image by transpose reads ----
+    // lane (g, i) of a 16-lane group reads 4 bf16 of row 4g + i/4 (and 16 + ...)
+    // at columns n0 + 4*(i%4); the hardware hands lane i column n0 + i.
+    const int rd_row0 = 4 * g4 + (h >> 2);
+    const int rd_col = 4 * (h & 3);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      typedef s16x4 __attribute__((address_space(3))) * lds_s16x4_ptr;
+      const uint32_t off0 = (uint32_t)(rd_row0 * LDS_ROW + (16 * dt + rd_col) * 2);
+      const uint32_t off1 = off0 + 16 * LDS_ROW;
+      __attribute__((address_space(3))) uint8_t* base =
+          (__attribute__((address_space(3))) uint8_t*)(lds);
+      s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(base + off0));
+      s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(base + off1));
+      u32x2 w0 = __builtin_bit_cast(u32x2, v0), w1 = __builtin_bit_cast(u32x2, v1);
+      u32x4 va = {w0[0], w0[1], w1[0], w1[1]};
+      o[dt] = mfma16(va, pb, o[dt]);
+    }
+    // the next tile's V overwrites this slice: LDS ops of one wave run in order
+    if (t1 < t_end) cur = nxt;
+  }
+
+  // ---- merge: 4 lanes per head within the wave (l is lane-partial) ----
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+
+  // ---- merge the 4 waves through LDS ----
+  __syncthreads();                               // all V slices consumed
+  float* sm_o = reinterpret_cast<float*>(smem);  // [kWaves][16][D]
+  float* sm_ml = sm_o + kWaves * 16 * D;         // [kWaves][16][2]
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sm_o[(w * 16 + h) * D + 16 * dt + 4 * g4 + r] = o[dt][r];
+  if (g4 == 0) { sm_ml[(w * 16 + h) * 2] = m; sm_ml[(w * 16 + h) * 2 + 1] = l; }
+  __syncthreads();
+  for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
+    const int hh = i / D, d = i - hh * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, sm_ml[(ww * 16 + hh) * 2]);
+    float lt = 0.0f, at = 0.0f;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) {
+      const float mw = sm_ml[(ww * 16 + hh) * 2];
+      const float f = (mw == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
+      lt = fmaf(sm_ml[(ww * 16 + hh) * 2 + 1], f, lt);
+      at = fmaf(sm_o[(ww * 16 + hh) * D + d], f, at);
+    }
+    const int hq = j * G + hh;
+    if (n_split == 1) {
+      static_cast<uint16_t*>(a.out)[(qrow * Hq + hq) * D + d] = f32_to_bf16_rne(at * vscale / lt);
+      if (d == 0 && a.lse) a.lse[qrow * Hq + hq] = (M + __log2f(lt)) * kLn2;
+    } else {
+      const size_t slot = ((size_t)z * Hq + hq) * a.max_splits + split;
+      a.ws_acc[slot * D + d] = at * vscale;
+      if (d == 0) { a.ws_ml[slot * 2] = M; a.ws_ml[slot * 2 + 1] = lt; }
+    }
+  }
+}
+
+}  // namespace
+
+bool decode_mfma_supported(const AttnArgs& a) {
+  const int G = a.num_q_heads / a.c.num_kv_heads;
+  return !a.prefill && G >= 3 && G <= 16 && a.c.kv_dtype != KV_F32 &&
+         (a.c.head_dim == 64 || a.c.head_dim == 128);
+}
+
+hipError_t launch_decode_partial_mfma(const AttnArgs& a, hipStream_t s) {
+  const dim3 grid(a.c.num_kv_heads, a.max_splits, a.num_rows), block(256);
+  if (a.c.kv_dtype == KV_BF16) {
+    if (a.c.head_dim == 128) hipLaunchKernelGGL((decode_partial_mfma<KV_BF16, 128>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((decode_partial_mfma<KV_BF16, 64>), grid, block, 0, s, a);
+  } else {
+    if (a.c.head_dim == 128) hipLaunchKernelGGL((decode_partial_mfma<KV_FP8, 128>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((decode_partial_mfma<KV_FP8, 64>), grid, block, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pkv

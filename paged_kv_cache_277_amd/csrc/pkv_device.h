@@ -51,6 +51,15 @@ __device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* o) {
   o[0] = lo.x; o[1] = lo.y; o[2] = hi.x; o[3] = hi.y;
 }
 
+// Two fp8 e4m3fn codes (bytes 2*HI, 2*HI+1 of w) -> two bf16 packed in a dword
+// (exact: every e4m3fn value is a bf16 value).
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  typedef __bf16 bf16x2_t __attribute__((__vector_size__(4)));
+  bf16x2_t r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(int(w), 1.0f, HI);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
 // float32 -> e4m3fn code.
 //   |y| >= 448 (or inf)      -> 448 with y's sign (saturation)
 //   2^-6 <= |y| < 448 (normal): keep exponent E, round the 23-bit mantissa to

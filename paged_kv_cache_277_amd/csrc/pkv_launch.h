@@ -56,6 +56,9 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 hipError_t launch_decode_partial(const AttnArgs& a, hipStream_t s);
 hipError_t launch_lse_merge(const AttnArgs& a, hipStream_t s);
 hipError_t launch_prefill(const AttnArgs& a, hipStream_t s);
+// Grouped-query decode on the matrix cores (G >= 3, bf16 or fp8 KV).
+bool decode_mfma_supported(const AttnArgs& a);
+hipError_t launch_decode_partial_mfma(const AttnArgs& a, hipStream_t s);
 hipError_t launch_fp8_to_f32(const uint8_t* codes, float* out, int64_t n, hipStream_t s);
 
 }  // namespace pkv

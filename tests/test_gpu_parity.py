@@ -150,6 +150,9 @@ DECODE_CASES = [
     ((5, 100), 16, 1, 64, 32, "bf16"),                    # G 16
     ((5, 100, 333), 8, 1, 64, 16, "fp8"),
     ((2, 3, 40), 4, 1, 128, 16, "f32"),
+    ((1, 31, 200), 4, 2, 128, 32, "fp8"),                 # G 2: fp8 on the vector path
+    ((1, 31, 200), 12, 4, 128, 32, "fp8"),                # G 3: smallest matrix-core group
+    ((17, 250), 48, 4, 64, 64, "bf16"),                   # G 12, D 64
 ]
 
 
