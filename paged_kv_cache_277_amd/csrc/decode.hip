@@ -407,10 +407,12 @@ hipError_t launch_lse_merge(const AttnArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Chunked prefill, generic path: every chunk row is a decode query over its
-// causal prefix (keys 0 .. ctx_before + i), one context range per row.
+// Chunked prefill.  bf16 queries go to the matrix-core kernel; the generic
+// path (fp32) treats every chunk row as a decode query over its causal prefix
+// (keys 0 .. ctx_before + i), one context range per row.
 hipError_t launch_prefill(const AttnArgs& a, hipStream_t s) {
   if (a.num_rows == 0 || a.max_chunk == 0) return hipSuccess;
+  if (prefill_mfma_supported(a)) return launch_prefill_mfma(a, s);
   const dim3 grid(a.c.num_kv_heads, 1, a.num_rows * a.max_chunk);
   return launch_vec_any(a, grid, s);
 }

@@ -59,6 +59,9 @@ hipError_t launch_prefill(const AttnArgs& a, hipStream_t s);
 // Grouped-query decode on the matrix cores (G >= 3, bf16 or fp8 KV).
 bool decode_mfma_supported(const AttnArgs& a);
 hipError_t launch_decode_partial_mfma(const AttnArgs& a, hipStream_t s);
+// Chunked prefill on the matrix cores (bf16 queries, bf16 or fp8 KV).
+bool prefill_mfma_supported(const AttnArgs& a);
+hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t s);
 hipError_t launch_fp8_to_f32(const uint8_t* codes, float* out, int64_t n, hipStream_t s);
 
 }  // namespace pkv

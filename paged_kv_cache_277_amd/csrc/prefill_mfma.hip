@@ -1,0 +1,310 @@
+// Chunked prefill on the matrix cores.
+//
+// Method: a context chunk of C new tokens of request r (already appended to
+// its pages after P_r cached tokens) attends causally: chunk row i, at
+// absolute position P_r + i, sees keys 0 .. P_r + i through the request's
+// block table ("TensorRT-LLM框架解析与高性能推理优化实践" §5.3 分块上下文处理; causal
+// mask and scaled dot-product attention of the fused-MHA pseudocode in
+// "TensorRT-LLM性能调优：提升LLM推理效率"; running max / sum, §6.1).
+//
+// Work decomposition (MI355X): the G query heads that share KV head j, times
+// the chunk's tokens, form "rows" (row = token*G + head).  A workgroup owns 64
+// consecutive rows of one (request, KV head) — 16 per wave, one MFMA N-tile —
+// and walks the keys 0 .. (its last row's position) in 32-token tiles.  Each
+// K/V tile is fetched from the pages once per workgroup into LDS (double
+// buffered: the next tile's global loads are in flight while the current
+// tile is computed) and shared by the four waves:
+//
+//   S^T[t][row] = sum_d K[t][d] Q[row][d]    A = K from LDS (16-byte reads),
+//                                            B = Q^T in registers
+//   O^T[d][row] += sum_t V[t][d] P^T[t][row] A = V^T by LDS transpose reads,
+//                                            B = P^T straight from S^T's layout
+//
+// with the operand layouts described in decode_mfma.hip.  LDS rows are
+// padded (K by 16 bytes, V by 32) so that the 16-byte K reads and the
+// transpose reads of V hit distinct banks.  Workgroups that share a
+// (request, KV head) — and so the same K/V tiles — are mapped to the same
+// XCD so those tiles are served from that XCD's L2.
+#include <math.h>
+
+#include "pkv_device.h"
+#include "pkv_launch.h"
+
+namespace pkv {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kRows = 16 * kWaves;          // rows per workgroup
+constexpr int kTile = 32;                   // keys per tile
+
+typedef __bf16 bf16x8_t __attribute__((__vector_size__(16)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return uint32_t(f32_to_bf16_rne(a)) | (uint32_t(f32_to_bf16_rne(b)) << 16);
+}
+
+template <int KVT, int D>
+struct PfShape {
+  static constexpr int KVB = KvBytes<KVT>::value;
+  static constexpr int ROWB = D * KVB;                     // pool bytes per token row
+  static constexpr int PIECES = kTile * ROWB / 16;         // 16-byte pieces per K (or V) tile
+  static constexpr int PPT = (PIECES + 255) / 256;         // pieces per thread per tile
+  static constexpr int K_LDS = D * 2 + 16;                 // padded bf16 rows in LDS
+  static constexpr int V_LDS = D * 2 + 32;
+  static constexpr int STAGE = kTile * (K_LDS + V_LDS);    // one buffer (K + V)
+  static_assert(PIECES % 256 == 0 || PIECES < 256, "tile must split evenly over the workgroup");
+};
+
+// Global loads of one K/V tile (pool storage format) into registers.
+template <int KVT, int D>
+struct PfRegs {
+  u32x4 k[PfShape<KVT, D>::PPT];
+  u32x4 v[PfShape<KVT, D>::PPT];
+};
+
+template <int KVT, int D>
+__device__ __forceinline__ void pf_load(PfRegs<KVT, D>& r, const uint8_t* kp, const uint8_t* vp,
+                                        const int32_t* btrow, int t0, int kmax, int Hkv, int j,
+                                        int pshift) {
+  using S = PfShape<KVT, D>;
+  constexpr int PR = S::ROWB / 16;                          // pieces per row
+  const int pmask = (1 << pshift) - 1;
+#pragma unroll
+  for (int i = 0; i < S::PPT; ++i) {
+    const int piece = threadIdx.x + 256 * i;
+    const int tok = piece / PR, pc = piece % PR;
+    const int t = t0 + tok;
+    if (piece < S::PIECES && t < kmax) {
+      const int page = btrow[t >> pshift];
+      const size_t off = ((((size_t)page * Hkv + j) << pshift | (size_t)(t & pmask)) * S::ROWB) +
+                         (size_t)pc * 16;
+      r.k[i] = ld16(kp + off);
+      r.v[i] = ld16(vp + off);
+    } else {
+      r.k[i] = u32x4{0, 0, 0, 0};
+      r.v[i] = u32x4{0, 0, 0, 0};
+    }
+  }
+}
+
+// Registers -> LDS (bf16 rows, padded).
+template <int KVT, int D>
+__device__ __forceinline__ void pf_store(const PfRegs<KVT, D>& r, uint8_t* kl, uint8_t* vl) {
+  using S = PfShape<KVT, D>;
+  constexpr int PR = S::ROWB / 16;
+#pragma unroll
+  for (int i = 0; i < S::PPT; ++i) {
+    const int piece = threadIdx.x + 256 * i;
+    const int tok = piece / PR, pc = piece % PR;
+    if (piece >= S::PIECES) continue;
+    if constexpr (KVT == KV_FP8) {
+      u32x4 klo, khi, vlo, vhi;
+      klo[0] = fp8x2_to_bf16x2<false>(r.k[i][0]); klo[1] = fp8x2_to_bf16x2<true>(r.k[i][0]);
+      klo[2] = fp8x2_to_bf16x2<false>(r.k[i][1]); klo[3] = fp8x2_to_bf16x2<true>(r.k[i][1]);
+      khi[0] = fp8x2_to_bf16x2<false>(r.k[i][2]); khi[1] = fp8x2_to_bf16x2<true>(r.k[i][2]);
+      khi[2] = fp8x2_to_bf16x2<false>(r.k[i][3]); khi[3] = fp8x2_to_bf16x2<true>(r.k[i][3]);
+      vlo[0] = fp8x2_to_bf16x2<false>(r.v[i][0]); vlo[1] = fp8x2_to_bf16x2<true>(r.v[i][0]);
+      vlo[2] = fp8x2_to_bf16x2<false>(r.v[i][1]); vlo[3] = fp8x2_to_bf16x2<true>(r.v[i][1]);
+      vhi[0] = fp8x2_to_bf16x2<false>(r.v[i][2]); vhi[1] = fp8x2_to_bf16x2<true>(r.v[i][2]);
+      vhi[2] = fp8x2_to_bf16x2<false>(r.v[i][3]); vhi[3] = fp8x2_to_bf16x2<true>(r.v[i][3]);
+      *reinterpret_cast<u32x4*>(kl + tok * S::K_LDS + pc * 32) = klo;
+      *reinterpret_cast<u32x4*>(kl + tok * S::K_LDS + pc * 32 + 16) = khi;
+      *reinterpret_cast<u32x4*>(vl + tok * S::V_LDS + pc * 32) = vlo;
+      *reinterpret_cast<u32x4*>(vl + tok * S::V_LDS + pc * 32 + 16) = vhi;
+    } else {
+      *reinterpret_cast<u32x4*>(kl + tok * S::K_LDS + pc * 16) = r.k[i];
+      *reinterpret_cast<u32x4*>(vl + tok * S::V_LDS + pc * 16) = r.v[i];
+    }
+  }
+}
+
+template <int KVT, int D>
+__global__ __launch_bounds__(256, 2) void prefill_mfma(AttnArgs a, int nqb) {
+  using S = PfShape<KVT, D>;
+  constexpr int KK = D / 32, DT = D / 16;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * S::STAGE];
+
+  const int Hq = a.num_q_heads, Hkv = a.c.num_kv_heads, G = Hq / Hkv;
+  // XCD-aware order: hardware places workgroup b on XCD b % 8; give each XCD
+  // a contiguous run of logical items so blocks of one (request, KV head) share L2.
+  const int nwg = gridDim.x;
+  const int b = blockIdx.x;
+  const int per = nwg / 8, extra = nwg % 8, xcd = b % 8, k = b / 8;
+  const int logical = (xcd < extra ? xcd * (per + 1) : extra * (per + 1) + (xcd - extra) * per) + k;
+  // logical -> (request-major, KV head, query block), last query blocks first
+  const int qb_rev = logical % nqb;
+  const int pair = logical / nqb;
+  const int j = pair % Hkv, r = pair / Hkv;
+  const int c0 = a.cu_q[r], C = a.cu_q[r + 1] - c0;
+  const int qb = nqb - 1 - qb_rev;
+  const int row0 = qb * kRows;                   // first flat row (token*G + head) of the block
+  if (row0 >= C * G) return;
+  const int Pr = a.ctx_before[r];
+  const int last_row = min(C * G, row0 + kRows) - 1;
+  const int kmax = Pr + last_row / G + 1;        // keys needed by the block's last row
+
+  const int lane = threadIdx.x & 63;
+  const int w = uniform(threadIdx.x >> 6);
+  const int g4 = lane >> 4, n = lane & 15;
+  const int my_row = row0 + 16 * w + n;          // this lane's row in S^T / O^T column n
+  const bool row_ok = my_row < C * G;
+  const int my_tok = my_row / G, my_head = my_row - my_tok * G;
+  const int my_lim = Pr + my_tok;                // last key this row may see
+  const int wave_last = min(C * G, row0 + 16 * w + 16) - 1;   // last real row of this wave
+  const int wave_kmax = wave_last >= row0 + 16 * w ? Pr + wave_last / G + 1 : 0;
+
+  float kscale = 1.0f, vscale = 1.0f;
+  if constexpr (KVT == KV_FP8) { kscale = a.c.k_scale[j]; vscale = a.c.v_scale[j]; }
+  const float smul = a.sm_scale * kLog2e * kscale;
+
+  // Q^T (B operand): lane (g4, n) holds Q[row n][g4*D/4 + 8kk + e].
+  u32x4 qb_reg[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) qb_reg[kk] = u32x4{0, 0, 0, 0};
+  if (row_ok) {
+    const uint16_t* q = static_cast<const uint16_t*>(a.q) +
+                        ((size_t)(c0 + my_tok) * Hq + (size_t)j * G + my_head) * D;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) qb_reg[kk] = ld16(q + (D / 4) * g4 + 8 * kk);
+  }
+
+  f32x4 o[DT];
+#pragma unroll
+  for (int i = 0; i < DT; ++i) o[i] = f32x4{0, 0, 0, 0};
+  float m = -INFINITY, l = 0.0f;
+
+  const int32_t* btrow = a.bt + (size_t)r * a.bt_stride;
+  const uint8_t* kp = static_cast<const uint8_t*>(a.c.k_pool);
+  const uint8_t* vp = static_cast<const uint8_t*>(a.c.v_pool);
+  const int ntiles = (kmax + kTile - 1) / kTile;
+  const int pshift = a.page_shift;
+
+  PfRegs<KVT, D> regs;
+  pf_load<KVT, D>(regs, kp, vp, btrow, 0, kmax, Hkv, j, pshift);
+  pf_store<KVT, D>(regs, smem, smem + kTile * S::K_LDS);
+  __syncthreads();
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int t0 = it * kTile;
+    uint8_t* kl = smem + (it & 1) * S::STAGE;
+    uint8_t* vl = kl + kTile * S::K_LDS;
+    if (it + 1 < ntiles) pf_load<KVT, D>(regs, kp, vp, btrow, t0 + kTile, kmax, Hkv, j, pshift);
+
+    if (t0 < wave_kmax) {                        // skip tiles wholly above this wave's diagonal
+      // ---- S^T for the two 16-key blocks ----
+      f32x4 s[2];
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        f32x4 acc = {0, 0, 0, 0};
+        const uint8_t* krow = kl + (16 * blk + n) * S::K_LDS + g4 * (D / 4) * 2;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          const u32x4 ka = *reinterpret_cast<const u32x4*>(krow + 16 * kk);
+          acc = mfma16(ka, qb_reg[kk], acc);
+        }
+        s[blk] = acc;
+      }
+      float sv[8];
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int t = t0 + 16 * blk + 4 * g4 + rr;
+          sv[4 * blk + rr] = (t <= my_lim) ? s[blk][rr] * smul : -INFINITY;
+        }
+      float mx = sv[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      // Key 0 is visible to every row, so after the first tile m is finite;
+      // padding rows (row_ok false) see key 0 too and stay finite.
+      const float mn = fmaxf(m, mx);
+      const float alpha = (mn == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m - mn);
+      m = mn;
+      float p[8], psum = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        p[i] = (mn == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sv[i] - mn);
+        psum += p[i];
+      }
+      l = l * alpha + psum;
+#pragma unroll
+      for (int i = 0; i < DT; ++i) o[i] *= alpha;
+      u32x4 pb;
+      pb[0] = pack_bf16x2(p[0], p[1]);
+      pb[1] = pack_bf16x2(p[2], p[3]);
+      pb[2] = pack_bf16x2(p[4], p[5]);
+      pb[3] = pack_bf16x2(p[6], p[7]);
+      // ---- O^T += V^T P^T ----
+      const int rd_row0 = 4 * g4 + (n >> 2);
+      const int rd_col = 4 * (n & 3);
+      typedef s16x4 __attribute__((address_space(3))) * lds_s16x4_ptr;
+      __attribute__((address_space(3))) uint8_t* vbase = (__attribute__((address_space(3))) uint8_t*)(vl);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const uint32_t off0 = (uint32_t)(rd_row0 * S::V_LDS + (16 * dt + rd_col) * 2);
+        const uint32_t off1 = off0 + 16 * S::V_LDS;
+        s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(vbase + off0));
+        s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(vbase + off1));
+        u32x2 w0 = __builtin_bit_cast(u32x2, v0), w1 = __builtin_bit_cast(u32x2, v1);
+        const u32x4 va = {w0[0], w0[1], w1[0], w1[1]};
+        o[dt] = mfma16(va, pb, o[dt]);
+      }
+    }
+    if (it + 1 < ntiles) {
+      uint8_t* kn = smem + ((it + 1) & 1) * S::STAGE;
+      pf_store<KVT, D>(regs, kn, kn + kTile * S::K_LDS);
+    }
+    __syncthreads();
+  }
+
+  // ---- finish rows: l is split over the 4 lanes of a row ----
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  if (row_ok) {
+    const float inv = vscale / l;
+    uint16_t* out = static_cast<uint16_t*>(a.out) +
+                    ((size_t)(c0 + my_tok) * Hq + (size_t)j * G + my_head) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const uint32_t lo = pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv);
+      const uint32_t hi = pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv);
+      *reinterpret_cast<u32x2*>(out + 16 * dt + 4 * g4) = u32x2{lo, hi};
+    }
+    if (g4 == 0 && a.lse)
+      a.lse[(size_t)(c0 + my_tok) * Hq + (size_t)j * G + my_head] = (m + __log2f(l)) * kLn2;
+  }
+}
+
+}  // namespace
+
+bool prefill_mfma_supported(const AttnArgs& a) {
+  return a.prefill && a.c.kv_dtype != KV_F32 && (a.c.head_dim == 64 || a.c.head_dim == 128);
+}
+
+hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t s) {
+  const int G = a.num_q_heads / a.c.num_kv_heads;
+  const int nqb = (a.max_chunk * G + kRows - 1) / kRows;
+  const long long nwg = (long long)nqb * a.c.num_kv_heads * a.num_rows;
+  if (nwg == 0) return hipSuccess;
+  if (nwg > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)nwg), block(256);
+  if (a.c.kv_dtype == KV_BF16) {
+    if (a.c.head_dim == 128) hipLaunchKernelGGL((prefill_mfma<KV_BF16, 128>), grid, block, 0, s, a, nqb);
+    else hipLaunchKernelGGL((prefill_mfma<KV_BF16, 64>), grid, block, 0, s, a, nqb);
+  } else {
+    if (a.c.head_dim == 128) hipLaunchKernelGGL((prefill_mfma<KV_FP8, 128>), grid, block, 0, s, a, nqb);
+    else hipLaunchKernelGGL((prefill_mfma<KV_FP8, 64>), grid, block, 0, s, a, nqb);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pkv

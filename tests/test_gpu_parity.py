@@ -238,6 +238,9 @@ PREFILL_CASES = [
     ((9,), 4, 4, 64, 16, "f32", (0, 5), 17),
     ((9,), 16, 2, 128, 64, "fp8", (64, 1), 70),
     ((9,), 8, 8, 64, 16, "bf16", (7,), 1),                    # single-token chunk
+    ((9,), 12, 4, 64, 16, "bf16", (3, 40), 33),               # G 3, page 16, ragged tiles
+    ((9,), 16, 16, 128, 64, "bf16", (100,), 77),              # G 1 on the matrix cores
+    ((9,), 8, 1, 64, 32, "fp8", (31,), 45),                   # G 8, fp8, head_dim 64
 ]
 
 
