@@ -174,7 +174,8 @@ pkv_status pkv_kv_cache_append(const pkv_cache_desc* cache,
  * context_lens : device int32[num_seqs], 0 <= L <= min(max_context_len,
  *                bt_stride * page_size); L counts the query's own token.
  *                L = 0 gives out = 0 and lse = -inf.
- * sm_scale     : score scale (1/sqrt(head_dim) for standard attention).
+ * sm_scale     : score scale, finite and > 0 (1/sqrt(head_dim) for standard
+ *                attention).
  * split_tokens : context range per work item, a positive multiple of
  *                page_size; 0 selects pkv_decode_split_tokens().
  * workspace    : device scratch of at least pkv_decode_workspace_bytes(...)

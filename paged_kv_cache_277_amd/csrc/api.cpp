@@ -160,7 +160,8 @@ pkv_status prepare_decode(const pkv_cache_desc* cache, const void* q, int32_t q_
       return fail(PKV_ERR_INVALID_ARG, "max_context_len %d exceeds bt_stride*page_size %lld",
                   max_context_len, (long long)bt_stride * cache->page_size);
   }
-  if (!std::isfinite(sm_scale)) return fail(PKV_ERR_INVALID_ARG, "sm_scale is not finite");
+  if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f))
+    return fail(PKV_ERR_INVALID_ARG, "sm_scale must be finite and positive");
   int32_t split;
   if ((st = resolve_split(cache, num_seqs, max_context_len, split_tokens, &split)) != PKV_OK)
     return st;
@@ -316,7 +317,8 @@ pkv_status pkv_paged_attn_chunked_prefill(const pkv_cache_desc* cache, const voi
   if ((st = check_heads(cache, num_q_heads)) != PKV_OK) return st;
   if (num_reqs < 0 || num_q_tokens < 0 || max_chunk_len < 0)
     return fail(PKV_ERR_INVALID_ARG, "negative size");
-  if (!std::isfinite(sm_scale)) return fail(PKV_ERR_INVALID_ARG, "sm_scale is not finite");
+  if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f))
+    return fail(PKV_ERR_INVALID_ARG, "sm_scale must be finite and positive");
   if (num_q_tokens == 0 || num_reqs == 0) return PKV_OK;
   if (!q || !out || !cu_q_lens || !ctx_before || !block_tables)
     return fail(PKV_ERR_INVALID_ARG, "prefill pointers must not be NULL");

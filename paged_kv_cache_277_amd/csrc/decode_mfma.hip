@@ -63,9 +63,6 @@ __device__ __forceinline__ void fp8x16_to_bf16(const u32x4& x, u32x4& lo, u32x4&
   hi[2] = fp8x2_to_bf16x2<false>(x[3]); hi[3] = fp8x2_to_bf16x2<true>(x[3]);
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return uint32_t(f32_to_bf16_rne(a)) | (uint32_t(f32_to_bf16_rne(b)) << 16);
-}
 
 // Per-lane register image of one 32-token tile.
 //   K: for each 16-token block, the lane's 32 d-values of token l%16 as bf16
@@ -120,7 +117,7 @@ __global__ __launch_bounds__(256, 2) void decode_partial_mfma(AttnArgs a) {
   constexpr int DT = D / 16;                    // 16-wide d tiles of the output
   constexpr int ROWB = TR::VROWB;
   constexpr int R = ROWB / 16, RPI = 64 / R, LPB = TR::VLOADS / 2;
-  constexpr int LDS_ROW = D * 2;                // bf16 V rows in LDS
+  constexpr int LDS_ROW = D * 2 + 32;           // bf16 V rows in LDS, padded against bank conflicts
   constexpr int STAGE_BYTES = kWaves * kTile * LDS_ROW;
   constexpr int MERGE_BYTES = (kWaves * 16 * D + kWaves * 32) * 4;
   __shared__ __attribute__((aligned(16)))
@@ -239,24 +236,27 @@ __global__ __launch_bounds__(256, 2) void decode_partial_mfma(AttnArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int tok = 16 * blk + 4 * g4 + r;
-        const float x = s[blk][r] * smul;
-        sv[4 * blk + r] = (full || t0 + tok < t_end) ? x : -INFINITY;
+        sv[4 * blk + r] = (full || t0 + tok < t_end) ? s[blk][r] : -INFINITY;
       }
     float mx = sv[0];
 #pragma unroll
     for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mn = fmaxf(m, mx);               // finite: every tile has a valid token
-    const float alpha = __builtin_amdgcn_exp2f(m - mn);
-    m = mn;
+    const float mn = fmaxf(m, mx * smul);        // finite: every tile has a valid token
+    if (__any(mn > m)) {                         // rescale only when some head's max grew
+      const float alpha = __builtin_amdgcn_exp2f(m - mn);
+      l *= alpha;
+#pragma unroll
+      for (int i = 0; i < DT; ++i) o[i] *= alpha;
+      m = mn;
+    }
     float p[8];
-    float psum = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) { p[i] = __builtin_amdgcn_exp2f(sv[i] - mn); psum += p[i]; }
-    l = l * alpha + psum;
-#pragma unroll
-    for (int i = 0; i < DT; ++i) o[i] *= alpha;
+    for (int i = 0; i < 8; ++i) {
+      p[i] = __builtin_amdgcn_exp2f(fmaf(sv[i], smul, -m));
+      l += p[i];
+    }
     u32x4 pb;                                    // P^T as B operand (token order above)
     pb[0] = pack_bf16x2(p[0], p[1]);
     pb[1] = pack_bf16x2(p[2], p[3]);

@@ -44,6 +44,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return uint16_t(u >> 16);
 }
 
+// Two floats -> packed bf16 pair (low = a), round to nearest even
+// (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef float f2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
+  const f2_t x = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, b2_t));
+}
+
 // Four fp8 e4m3fn codes (one dword, byte 0 first) -> four floats.
 __device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* o) {
   f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(int(w), false);

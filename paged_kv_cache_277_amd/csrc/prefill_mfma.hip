@@ -11,9 +11,10 @@
 // the chunk's tokens, form "rows" (row = token*G + head).  A workgroup owns 64
 // consecutive rows of one (request, KV head) — 16 per wave, one MFMA N-tile —
 // and walks the keys 0 .. (its last row's position) in 32-token tiles.  Each
-// K/V tile is fetched from the pages once per workgroup into LDS (double
-// buffered: the next tile's global loads are in flight while the current
-// tile is computed) and shared by the four waves:
+// K/V tile is fetched from the pages once per workgroup into LDS and shared by
+// the four waves; loads run two tiles ahead of the compute (register
+// staging, double-buffered LDS), with the request's block-table entries
+// staged in LDS so no load waits on another:
 //
 //   S^T[t][row] = sum_d K[t][d] Q[row][d]    A = K from LDS (16-byte reads),
 //                                            B = Q^T in registers
@@ -36,6 +37,7 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kRows = 16 * kWaves;          // rows per workgroup
 constexpr int kTile = 32;                   // keys per tile
+constexpr int kMaxPages = 512;              // block-table entries staged per workgroup
 
 typedef __bf16 bf16x8_t __attribute__((__vector_size__(16)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -46,9 +48,6 @@ __device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, const f3
                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return uint32_t(f32_to_bf16_rne(a)) | (uint32_t(f32_to_bf16_rne(b)) << 16);
-}
 
 template <int KVT, int D>
 struct PfShape {
@@ -71,7 +70,7 @@ struct PfRegs {
 
 template <int KVT, int D>
 __device__ __forceinline__ void pf_load(PfRegs<KVT, D>& r, const uint8_t* kp, const uint8_t* vp,
-                                        const int32_t* btrow, int t0, int kmax, int Hkv, int j,
+                                        const int32_t* pages, int t0, int kmax, int Hkv, int j,
                                         int pshift) {
   using S = PfShape<KVT, D>;
   constexpr int PR = S::ROWB / 16;                          // pieces per row
@@ -82,7 +81,7 @@ __device__ __forceinline__ void pf_load(PfRegs<KVT, D>& r, const uint8_t* kp, co
     const int tok = piece / PR, pc = piece % PR;
     const int t = t0 + tok;
     if (piece < S::PIECES && t < kmax) {
-      const int page = btrow[t >> pshift];
+      const int page = pages[t >> pshift];
       const size_t off = ((((size_t)page * Hkv + j) << pshift | (size_t)(t & pmask)) * S::ROWB) +
                          (size_t)pc * 16;
       r.k[i] = ld16(kp + off);
@@ -129,21 +128,22 @@ template <int KVT, int D>
 __global__ __launch_bounds__(256, 2) void prefill_mfma(AttnArgs a, int nqb) {
   using S = PfShape<KVT, D>;
   constexpr int KK = D / 32, DT = D / 16;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * S::STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * S::STAGE + kMaxPages * 4];
 
   const int Hq = a.num_q_heads, Hkv = a.c.num_kv_heads, G = Hq / Hkv;
-  // XCD-aware order: hardware places workgroup b on XCD b % 8; give each XCD
-  // a contiguous run of logical items so blocks of one (request, KV head) share L2.
-  const int nwg = gridDim.x;
+  // XCD-aware order: the hardware places workgroup b on XCD b % 8.  Pair
+  // p = (request, KV head) goes to XCD p % 8 — all query blocks of a pair
+  // share that XCD's L2, and consecutive pairs (the heads of one request)
+  // spread over all XCDs so no XCD gets one request's whole load.  Grid size
+  // is 8 * ceil(pairs / 8) * nqb; ids past the last pair exit.
   const int b = blockIdx.x;
-  const int per = nwg / 8, extra = nwg % 8, xcd = b % 8, k = b / 8;
-  const int logical = (xcd < extra ? xcd * (per + 1) : extra * (per + 1) + (xcd - extra) * per) + k;
-  // logical -> (request-major, KV head, query block), last query blocks first
-  const int qb_rev = logical % nqb;
-  const int pair = logical / nqb;
+  const int xcd = b % 8, k = b / 8;
+  const int pair = (k / nqb) * 8 + xcd;
+  const int qb_rev = k % nqb;
+  if (pair >= a.num_rows * Hkv) return;
   const int j = pair % Hkv, r = pair / Hkv;
   const int c0 = a.cu_q[r], C = a.cu_q[r + 1] - c0;
-  const int qb = nqb - 1 - qb_rev;
+  const int qb = nqb - 1 - qb_rev;               // later (heavier) query blocks first
   const int row0 = qb * kRows;                   // first flat row (token*G + head) of the block
   if (row0 >= C * G) return;
   const int Pr = a.ctx_before[r];
@@ -159,6 +159,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma(AttnArgs a, int nqb) {
   const int my_lim = Pr + my_tok;                // last key this row may see
   const int wave_last = min(C * G, row0 + 16 * w + 16) - 1;   // last real row of this wave
   const int wave_kmax = wave_last >= row0 + 16 * w ? Pr + wave_last / G + 1 : 0;
+  const int wave_min_lim = Pr + (row0 + 16 * w) / G;           // smallest key limit in the wave
 
   float kscale = 1.0f, vscale = 1.0f;
   if constexpr (KVT == KV_FP8) { kscale = a.c.k_scale[j]; vscale = a.c.v_scale[j]; }
@@ -186,16 +187,26 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma(AttnArgs a, int nqb) {
   const int ntiles = (kmax + kTile - 1) / kTile;
   const int pshift = a.page_shift;
 
-  PfRegs<KVT, D> regs;
-  pf_load<KVT, D>(regs, kp, vp, btrow, 0, kmax, Hkv, j, pshift);
-  pf_store<KVT, D>(regs, smem, smem + kTile * S::K_LDS);
+  // The request's block-table entries for keys 0..kmax-1, staged in LDS once.
+  int32_t* pages = reinterpret_cast<int32_t*>(smem + 2 * S::STAGE);
+  const int npages = (kmax + (1 << pshift) - 1) >> pshift;
+  for (int i = threadIdx.x; i < npages; i += blockDim.x) pages[i] = btrow[i];
   __syncthreads();
 
-  for (int it = 0; it < ntiles; ++it) {
+  // Pipeline: tile t is staged in register set t % 2 and LDS buffer t % 2.
+  // While tile i is computed, the loads of tile i+2 are in flight and tile
+  // i+1 (loaded one step earlier) is written to the other LDS buffer.
+  PfRegs<KVT, D> r0, r1;
+  pf_load<KVT, D>(r0, kp, vp, pages, 0, kmax, Hkv, j, pshift);
+  if (ntiles > 1) pf_load<KVT, D>(r1, kp, vp, pages, kTile, kmax, Hkv, j, pshift);
+  pf_store<KVT, D>(r0, smem, smem + kTile * S::K_LDS);
+  __syncthreads();
+
+  auto step = [&](int it, PfRegs<KVT, D>& rfree, const PfRegs<KVT, D>& rnext) {
     const int t0 = it * kTile;
     uint8_t* kl = smem + (it & 1) * S::STAGE;
     uint8_t* vl = kl + kTile * S::K_LDS;
-    if (it + 1 < ntiles) pf_load<KVT, D>(regs, kp, vp, btrow, t0 + kTile, kmax, Hkv, j, pshift);
+    if (it + 2 < ntiles) pf_load<KVT, D>(rfree, kp, vp, pages, t0 + 2 * kTile, kmax, Hkv, j, pshift);
 
     if (t0 < wave_kmax) {                        // skip tiles wholly above this wave's diagonal
       // ---- S^T for the two 16-key blocks ----
@@ -211,33 +222,41 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma(AttnArgs a, int nqb) {
         }
         s[blk] = acc;
       }
+      // Raw scores; the causal mask only matters on tiles that cross this
+      // wave's diagonal.  The scale enters the exponent as one FMA.
       float sv[8];
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int t = t0 + 16 * blk + 4 * g4 + rr;
-          sv[4 * blk + rr] = (t <= my_lim) ? s[blk][rr] * smul : -INFINITY;
-        }
+        for (int rr = 0; rr < 4; ++rr) sv[4 * blk + rr] = s[blk][rr];
+      if (t0 + kTile - 1 > wave_min_lim) {
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+            if (t0 + 16 * blk + 4 * g4 + rr > my_lim) sv[4 * blk + rr] = -INFINITY;
+      }
       float mx = sv[0];
 #pragma unroll
       for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      // Key 0 is visible to every row, so after the first tile m is finite;
-      // padding rows (row_ok false) see key 0 too and stay finite.
-      const float mn = fmaxf(m, mx);
-      const float alpha = (mn == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m - mn);
-      m = mn;
-      float p[8], psum = 0.0f;
+      // Key 0 is visible to every row (padding rows included), so mx is
+      // finite on the first tile and m stays finite afterwards.
+      const float mn = fmaxf(m, mx * smul);
+      if (__any(mn > m)) {                       // rescale only when some row's max grew
+        const float alpha = __builtin_amdgcn_exp2f(m - mn);
+        l *= alpha;
+#pragma unroll
+        for (int i = 0; i < DT; ++i) o[i] *= alpha;
+        m = mn;
+      }
+      float p[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        p[i] = (mn == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sv[i] - mn);
-        psum += p[i];
+        p[i] = __builtin_amdgcn_exp2f(fmaf(sv[i], smul, -m));
+        l += p[i];
       }
-      l = l * alpha + psum;
-#pragma unroll
-      for (int i = 0; i < DT; ++i) o[i] *= alpha;
       u32x4 pb;
       pb[0] = pack_bf16x2(p[0], p[1]);
       pb[1] = pack_bf16x2(p[2], p[3]);
@@ -261,9 +280,14 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma(AttnArgs a, int nqb) {
     }
     if (it + 1 < ntiles) {
       uint8_t* kn = smem + ((it + 1) & 1) * S::STAGE;
-      pf_store<KVT, D>(regs, kn, kn + kTile * S::K_LDS);
+      pf_store<KVT, D>(rnext, kn, kn + kTile * S::K_LDS);
     }
     __syncthreads();
+  };
+
+  for (int it = 0; it < ntiles; it += 2) {
+    step(it, r0, r1);
+    if (it + 1 < ntiles) step(it + 1, r1, r0);
   }
 
   // ---- finish rows: l is split over the 4 lanes of a row ----
@@ -287,13 +311,15 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma(AttnArgs a, int nqb) {
 }  // namespace
 
 bool prefill_mfma_supported(const AttnArgs& a) {
-  return a.prefill && a.c.kv_dtype != KV_F32 && (a.c.head_dim == 64 || a.c.head_dim == 128);
+  return a.prefill && a.c.kv_dtype != KV_F32 && (a.c.head_dim == 64 || a.c.head_dim == 128) &&
+         a.bt_stride <= kMaxPages;
 }
 
 hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t s) {
   const int G = a.num_q_heads / a.c.num_kv_heads;
   const int nqb = (a.max_chunk * G + kRows - 1) / kRows;
-  const long long nwg = (long long)nqb * a.c.num_kv_heads * a.num_rows;
+  const long long pairs = (long long)a.c.num_kv_heads * a.num_rows;
+  const long long nwg = (pairs + 7) / 8 * 8 * nqb;
   if (nwg == 0) return hipSuccess;
   if (nwg > 0x7FFFFFFFLL) return hipErrorInvalidValue;
   const dim3 grid((unsigned)nwg), block(256);

@@ -140,6 +140,8 @@ def test_decode_rejects_bad_arguments():
     assert _decode(d, split=24) == B.PKV_ERR_INVALID_ARG             # not a multiple of the page
     assert _decode(d, B_=-1) == B.PKV_ERR_INVALID_ARG
     assert _decode(d, scale=float("nan")) == B.PKV_ERR_INVALID_ARG
+    assert _decode(d, scale=-0.125) == B.PKV_ERR_INVALID_ARG
+    assert _decode(d, scale=0.0) == B.PKV_ERR_INVALID_ARG
     # two ranges of 32 need a workspace
     assert _decode(d, split=32, max_len=64) == B.PKV_ERR_INVALID_ARG
     assert b"workspace" in B.lib().pkv_last_error()
