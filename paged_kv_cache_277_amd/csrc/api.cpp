@@ -94,26 +94,39 @@ pkv::CacheView view(const pkv_cache_desc* c) {
 
 int32_t ceil_div(int64_t a, int64_t b) { return (int32_t)((a + b - 1) / b); }
 
-int32_t default_split(const pkv_cache_desc* c, int32_t num_seqs, int32_t max_len) {
-  // A work item reads about 256 KiB of K+V per KV head by default (512 tokens
-  // of 16-bit or 1024 of fp8 at head_dim 128); smaller ranges are used when
-  // the batch would otherwise give fewer than ~8 work items per CU.
+int32_t default_split(const pkv_cache_desc* c, int32_t num_seqs, int32_t num_q_heads,
+                      int32_t max_len) {
   const int gran = std::max(16, (int)c->page_size);
-  int split = c->kv_dtype == PKV_FP8_E4M3FN ? 1024 : 512;
-  if (c->head_dim == 64) split *= 2;
-  split = std::max(gran, split / gran * gran);
-  const int floor_split = std::max(gran, 256);   // below this the merge costs more than it hides
   const int64_t pairs = (int64_t)std::max(1, num_seqs) * c->num_kv_heads;
-  while (split / 2 >= floor_split && pairs * ceil_div(std::max(1, max_len), split) < 8 * kNumCUs)
-    split = std::max(gran, split / 2 / gran * gran);
+  const int G = num_q_heads / c->num_kv_heads;
+  int split;
+  if (G >= 3 && c->kv_dtype != PKV_F32) {
+    // Matrix-core path (2 waves/SIMD): long ranges amortise each work
+    // item's start-up, but the grid must keep ~2048 items.  With only the
+    // longest context known, the expected item count assumes contexts
+    // average half of it.  Ranges of 512..2048 tokens.
+    split = 512;
+    while (split < 2048 && pairs * ceil_div(std::max(1, max_len), 2 * split) / 2 >= 2048) split *= 2;
+  } else {
+    // Vector path: ~256 KiB of K+V per KV head and item (512 tokens of
+    // 16-bit or 1024 of fp8 at head_dim 128); shorter ranges when the batch
+    // would give fewer than ~8 items per CU, never below 256 tokens (the merge
+    // would cost more than the parallelism gains).
+    split = c->kv_dtype == PKV_FP8_E4M3FN ? 1024 : 512;
+    if (c->head_dim == 64) split *= 2;
+    const int floor_split = 256;
+    while (split / 2 >= floor_split && pairs * ceil_div(std::max(1, max_len), split) < 8 * kNumCUs)
+      split /= 2;
+  }
+  split = std::max(gran, split / gran * gran);
   if (max_len <= split) split = std::max(gran, ceil_div(std::max(1, max_len), gran) * gran);
   return split;
 }
 
-pkv_status resolve_split(const pkv_cache_desc* c, int32_t num_seqs, int32_t max_len,
-                         int32_t split_tokens, int32_t* out) {
+pkv_status resolve_split(const pkv_cache_desc* c, int32_t num_seqs, int32_t num_q_heads,
+                         int32_t max_len, int32_t split_tokens, int32_t* out) {
   if (split_tokens == 0) {
-    *out = default_split(c, num_seqs, max_len);
+    *out = default_split(c, num_seqs, num_q_heads, max_len);
     return PKV_OK;
   }
   if (split_tokens < 0 || split_tokens % c->page_size != 0 || split_tokens % 16 != 0)
@@ -163,7 +176,8 @@ pkv_status prepare_decode(const pkv_cache_desc* cache, const void* q, int32_t q_
   if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f))
     return fail(PKV_ERR_INVALID_ARG, "sm_scale must be finite and positive");
   int32_t split;
-  if ((st = resolve_split(cache, num_seqs, max_context_len, split_tokens, &split)) != PKV_OK)
+  if ((st = resolve_split(cache, num_seqs, num_q_heads, max_context_len, split_tokens, &split)) !=
+      PKV_OK)
     return st;
   const size_t need = workspace_bytes(cache, num_seqs, num_q_heads, max_context_len, split);
   if (need > 0 && (!workspace || workspace_bytes_in < need))
@@ -245,7 +259,7 @@ int32_t pkv_decode_split_tokens(const pkv_cache_desc* cache, int32_t num_seqs, i
                                 int32_t max_context_len) {
   if (check_cache(cache) != PKV_OK || check_heads(cache, num_q_heads) != PKV_OK) return 0;
   if (num_seqs < 0 || max_context_len < 0) return 0;
-  return default_split(cache, num_seqs, max_context_len);
+  return default_split(cache, num_seqs, num_q_heads, max_context_len);
 }
 
 size_t pkv_decode_workspace_bytes(const pkv_cache_desc* cache, int32_t num_seqs,
@@ -253,7 +267,8 @@ size_t pkv_decode_workspace_bytes(const pkv_cache_desc* cache, int32_t num_seqs,
                                   int32_t split_tokens) {
   if (check_cache(cache) != PKV_OK || check_heads(cache, num_q_heads) != PKV_OK) return 0;
   int32_t split;
-  if (resolve_split(cache, num_seqs, max_context_len, split_tokens, &split) != PKV_OK) return 0;
+  if (resolve_split(cache, num_seqs, num_q_heads, max_context_len, split_tokens, &split) != PKV_OK)
+    return 0;
   return workspace_bytes(cache, num_seqs, num_q_heads, max_context_len, split);
 }
 

@@ -81,18 +81,25 @@ struct TileRegs {
   u32x4 v[VLOADS];
 };
 
-template <int KVT, int D, bool MASKED>
+// Page ids of the two 16-token blocks of the tile at t0 (a block past the end
+// reuses the first block's page: in bounds, and masked later).
+__device__ __forceinline__ void tile_pages(const int32_t* btrow, int t0, int t_end, int pshift,
+                                           int& p0, int& p1) {
+  p0 = btrow[t0 >> pshift];
+  p1 = (t0 + 16 < t_end) ? btrow[(t0 + 16) >> pshift] : p0;
+}
+
+template <int KVT, int D>
 __device__ __forceinline__ void load_tile(TileRegs<KVT, D>& r, const uint8_t* kp, const uint8_t* vp,
-                                          const int32_t* btrow, int t0, int t_end, int Hkv, int j,
+                                          int p0, int p1, int t0, int t_end, int Hkv, int j,
                                           int pshift, int lane) {
   using TR = TileRegs<KVT, D>;
   constexpr int ROWB = TR::VROWB;
   const int pmask = (1 << pshift) - 1;
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
-    const int tb = t0 + 16 * blk;
-    // A block past the end reuses the first block's page (in bounds; masked later).
-    const int page = btrow[(MASKED && tb >= t_end ? t0 : tb) >> pshift];
+    const int tb = (blk == 1 && t0 + 16 >= t_end) ? t0 : t0 + 16 * blk;
+    const int page = blk == 0 ? p0 : p1;
     const size_t row = (((size_t)page * Hkv + j) << pshift | (size_t)(tb & pmask));
     // K: token (lane % 16), d-range [g*D/4, (g+1)*D/4)
     const uint8_t* kbase = kp + (row + (lane & 15)) * ROWB + (size_t)(lane >> 4) * TR::DPL * TR::KVB;
@@ -169,17 +176,24 @@ __global__ __launch_bounds__(256, 2) void decode_partial_mfma(AttnArgs a) {
   uint8_t* lds = smem + w * kTile * LDS_ROW;
   constexpr int STRIDE = kWaves * kTile;
 
+  // Ping-pong pipeline over this wave's tiles t0, t0+STRIDE, ...: while a
+  // tile is computed the next one's loads are in flight, and the page ids of
+  // the tile after that are already in registers.
   int t0 = t_begin + w * kTile;
-  TR cur, nxt;
+  TR bufA, bufB;
+  int pa0 = 0, pa1 = 0, pb0 = 0, pb1 = 0;
   if (t0 < t_end) {
-    if (t0 + kTile <= t_end) load_tile<KVT, D, false>(cur, kp, vp, btrow, t0, t_end, Hkv, j, pshift, lane);
-    else load_tile<KVT, D, true>(cur, kp, vp, btrow, t0, t_end, Hkv, j, pshift, lane);
+    tile_pages(btrow, t0, t_end, pshift, pa0, pa1);
+    load_tile<KVT, D>(bufA, kp, vp, pa0, pa1, t0, t_end, Hkv, j, pshift, lane);
+    if (t0 + STRIDE < t_end) tile_pages(btrow, t0 + STRIDE, t_end, pshift, pb0, pb1);
   }
-  for (; t0 < t_end; t0 += STRIDE) {
+  auto step = [&](TR& cur, TR& nxt, int& q0, int& q1, const int& n0, const int& n1) {
+    // cur: tile t0 (loaded); nxt: receives tile t0+STRIDE (pages n0/n1);
+    // q0/q1 receive the pages of tile t0+2*STRIDE.
     const int t1 = t0 + STRIDE;
     if (t1 < t_end) {
-      if (t1 + kTile <= t_end) load_tile<KVT, D, false>(nxt, kp, vp, btrow, t1, t_end, Hkv, j, pshift, lane);
-      else load_tile<KVT, D, true>(nxt, kp, vp, btrow, t1, t_end, Hkv, j, pshift, lane);
+      load_tile<KVT, D>(nxt, kp, vp, n0, n1, t1, t_end, Hkv, j, pshift, lane);
+      if (t1 + STRIDE < t_end) tile_pages(btrow, t1 + STRIDE, t_end, pshift, q0, q1);
     }
     const bool full = t0 + kTile <= t_end;
 
@@ -281,8 +295,13 @@ __global__ __launch_bounds__(256, 2) void decode_partial_mfma(AttnArgs a) {
       u32x4 va = {w0[0], w0[1], w1[0], w1[1]};
       o[dt] = mfma16(va, pb, o[dt]);
     }
-    // the next tile's V overwrites this slice: LDS ops of one wave run in order
-    if (t1 < t_end) cur = nxt;
+  };
+  while (t0 < t_end) {
+    step(bufA, bufB, pa0, pa1, pb0, pb1);
+    t0 += STRIDE;
+    if (t0 >= t_end) break;
+    step(bufB, bufA, pb0, pb1, pa0, pa1);
+    t0 += STRIDE;
   }
 
   // ---- merge: 4 lanes per head within the wave (l is lane-partial) ----
