@@ -196,8 +196,8 @@ __global__ __launch_bounds__(256) void decode_partial_vec(AttnArgs a) {
     const size_t base = tile_base(btrow[t0 >> pshift], t0);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      kA[u] = ld16(kp + base + (size_t)u * RW * ROWB);
-      vA[u] = ld16(vp + base + (size_t)u * RW * ROWB);
+      kA[u] = ld16_stream(kp + base + (size_t)u * RW * ROWB);
+      vA[u] = ld16_stream(vp + base + (size_t)u * RW * ROWB);
     }
     if (t0 + STRIDE < t_end) page_next = btrow[(t0 + STRIDE) >> pshift];
   }
@@ -208,8 +208,8 @@ __global__ __launch_bounds__(256) void decode_partial_vec(AttnArgs a) {
       const size_t base = tile_base(page_next, t1);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        kB[u] = ld16(kp + base + (size_t)u * RW * ROWB);
-        vB[u] = ld16(vp + base + (size_t)u * RW * ROWB);
+        kB[u] = ld16_stream(kp + base + (size_t)u * RW * ROWB);
+        vB[u] = ld16_stream(vp + base + (size_t)u * RW * ROWB);
       }
       if (t1 + STRIDE < t_end) page_next = btrow[(t1 + STRIDE) >> pshift];
     }

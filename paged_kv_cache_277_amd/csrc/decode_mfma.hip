@@ -13,11 +13,11 @@
 // Lane layouts of the 16x16x32 bf16 MFMA (wave64): A[i][k] in lane i%16 +
 // 16*(k/8), element k%8; B[k][j] in lane j + 16*(k/8); C[i][j] in lane
 // j + 16*(i/4), element i%4.  Consequences used below:
-//   * K rows go straight from HBM to the A operand: lane l reads 64
-//     contiguous bytes (bf16) or 32 (fp8) of token l%16 covering
-//     d in [32g, 32g+32), g = l/16; MFMA step kk uses d = 32g + 8kk + e.  The
-//     contraction over d is order-free, so Q^T (B operand) is loaded in the
-//     same d order.
+//   * K rows go straight from HBM to the A operand: lane l holds token l%16;
+//     its load i reads 16-byte piece 4i + g (g = l/16) of the row, so each load
+//     instruction reads 64 contiguous bytes of 16 rows.  For bf16, step kk
+//     uses d = 32kk + 8g + e; for fp8 (16 codes per piece) d = 64(kk/2) + 16g +
+//     8(kk%2) + e.  Q^T (B operand) is loaded in the same d order.
 //   * The S^T result leaves, in lane l, head h = l%16 for tokens 4g+r of each
 //     16-token block; over the two blocks of a tile that is 8 tokens of one
 //     head — exactly a B operand row of P^T if the tile's tokens are taken in
@@ -89,6 +89,15 @@ __device__ __forceinline__ void tile_pages(const int32_t* btrow, int t0, int t_e
   p1 = (t0 + 16 < t_end) ? btrow[(t0 + 16) >> pshift] : p0;
 }
 
+// First of the 8 consecutive d values that MFMA step kk takes for lane group g:
+// K load i of a lane holds 16-byte piece 4i + g of its token row, i.e. 8 bf16
+// (step kk = i) or 16 fp8 codes (steps 2i and 2i + 1).
+template <int KVT>
+__device__ __forceinline__ int k_elem_offset(int kk, int g) {
+  if constexpr (KVT == KV_FP8) return 64 * (kk >> 1) + 16 * g + 8 * (kk & 1);
+  else return 32 * kk + 8 * g;
+}
+
 template <int KVT, int D>
 __device__ __forceinline__ void load_tile(TileRegs<KVT, D>& r, const uint8_t* kp, const uint8_t* vp,
                                           int p0, int p1, int t0, int t_end, int Hkv, int j,
@@ -101,10 +110,11 @@ __device__ __forceinline__ void load_tile(TileRegs<KVT, D>& r, const uint8_t* kp
     const int tb = (blk == 1 && t0 + 16 >= t_end) ? t0 : t0 + 16 * blk;
     const int page = blk == 0 ? p0 : p1;
     const size_t row = (((size_t)page * Hkv + j) << pshift | (size_t)(tb & pmask));
-    // K: token (lane % 16), d-range [g*D/4, (g+1)*D/4)
-    const uint8_t* kbase = kp + (row + (lane & 15)) * ROWB + (size_t)(lane >> 4) * TR::DPL * TR::KVB;
+    // K: token (lane % 16); load i reads 16-byte piece 4i + g of the row, so
+    // one load instruction covers 64 contiguous bytes of each of 16 rows.
+    const uint8_t* kbase = kp + (row + (lane & 15)) * ROWB + (size_t)(lane >> 4) * 16;
 #pragma unroll
-    for (int i = 0; i < TR::KPL; ++i) r.k[blk][i] = ld16(kbase + 16 * i);
+    for (int i = 0; i < TR::KPL; ++i) r.k[blk][i] = ld16(kbase + 64 * i);
     // V: rows of this block, 16-byte pieces in row-major order
     constexpr int R = ROWB / 16;                 // lanes per row
     constexpr int RPI = 64 / R;                  // rows per load instruction
@@ -112,7 +122,7 @@ __device__ __forceinline__ void load_tile(TileRegs<KVT, D>& r, const uint8_t* kp
 #pragma unroll
     for (int i = 0; i < LPB; ++i) {
       const int rr = (lane / R) + RPI * i;       // row within the block (0..15)
-      r.v[blk * LPB + i] = ld16(vp + (row + rr) * ROWB + (size_t)(lane % R) * 16);
+      r.v[blk * LPB + i] = ld16_stream(vp + (row + rr) * ROWB + (size_t)(lane % R) * 16);
     }
   }
 }
@@ -155,14 +165,15 @@ __global__ __launch_bounds__(256, 2) void decode_partial_mfma(AttnArgs a) {
   if constexpr (KVT == KV_FP8) { kscale = a.c.k_scale[j]; vscale = a.c.v_scale[j]; }
   const float smul = a.sm_scale * kLog2e * kscale;
 
-  // Q^T as B operand: lane (g, h) holds Q[j*G + h][g*D/4 + 8kk + e]; zero for h >= G.
+  // Q^T as B operand: lane (g, h) holds Q[j*G + h][d] for the d's that MFMA
+  // step kk takes from K (k_elem_offset); zero for h >= G.
   u32x4 qb[KK];
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) qb[kk] = u32x4{0, 0, 0, 0};
   if (h < G) {
     const uint16_t* q = static_cast<const uint16_t*>(a.q) + (qrow * Hq + (size_t)j * G + h) * D;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) qb[kk] = ld16(q + (D / 4) * g4 + 8 * kk);
+    for (int kk = 0; kk < KK; ++kk) qb[kk] = ld16(q + k_elem_offset<KVT>(kk, g4));
   }
 
   f32x4 o[DT];

@@ -95,10 +95,16 @@ __device__ __forceinline__ uint32_t f32_to_e4m3fn(float y) {
   return sign | ((e << 3) + keep + up);
 }
 
-// 16 bytes from global memory (non-temporal hint off: K/V pages may be reused
-// by other work items through the shared prefix).
+// 16 bytes from global memory.
 __device__ __forceinline__ u32x4 ld16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
+}
+
+// 16 bytes with the non-temporal hint: for K/V rows that one pass reads once
+// (decode).  On MI355X streaming reads sustain markedly more bandwidth with
+// the hint than without it.
+__device__ __forceinline__ u32x4 ld16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
 // DPP lane moves within a row of 16 lanes (gfx9 DPP controls).
