@@ -64,20 +64,16 @@ __device__ __forceinline__ void fp8x16_to_bf16(const u32x4& x, u32x4& lo, u32x4&
 }
 
 
-// Per-lane register image of one 32-token tile.
-//   K: for each 16-token block, the lane's 32 d-values of token l%16 as bf16
-//      (KB = 4 u32x4 per block for bf16 storage; fp8 is loaded as 2 u32x4 and
-//      widened when used).
-//   V: row-major pieces for the LDS image: lane l holds 16-byte piece l%R of
-//      rows (l/R) + (64/R)*i.
+// Per-lane register image of one 32-token tile, K and V alike: lane l holds
+// the 16-byte pieces l%R of rows (l/R) + (64/R)*i of each 16-token block, so
+// every load instruction reads whole rows (64*16 contiguous bytes per block
+// row group) and can carry the streaming hint.
 template <int KVT, int D>
 struct TileRegs {
   static constexpr int KVB = KvBytes<KVT>::value;
-  static constexpr int DPL = D / 4;                    // d values per lane group
-  static constexpr int KPL = (DPL * KVB) / 16;         // K 16-byte loads per lane per block
-  static constexpr int VROWB = D * KVB;                // bytes per V row in the pool
-  static constexpr int VLOADS = (kTile * VROWB) / (64 * 16);  // V 16-byte loads per lane
-  u32x4 k[2][KPL];
+  static constexpr int VROWB = D * KVB;                // bytes per K/V row in the pool
+  static constexpr int VLOADS = (kTile * VROWB) / (64 * 16);  // 16-byte loads per lane, each of K and V
+  u32x4 k[VLOADS];
   u32x4 v[VLOADS];
 };
 
@@ -110,19 +106,16 @@ __device__ __forceinline__ void load_tile(TileRegs<KVT, D>& r, const uint8_t* kp
     const int tb = (blk == 1 && t0 + 16 >= t_end) ? t0 : t0 + 16 * blk;
     const int page = blk == 0 ? p0 : p1;
     const size_t row = (((size_t)page * Hkv + j) << pshift | (size_t)(tb & pmask));
-    // K: token (lane % 16); load i reads 16-byte piece 4i + g of the row, so
-    // one load instruction covers 64 contiguous bytes of each of 16 rows.
-    const uint8_t* kbase = kp + (row + (lane & 15)) * ROWB + (size_t)(lane >> 4) * 16;
-#pragma unroll
-    for (int i = 0; i < TR::KPL; ++i) r.k[blk][i] = ld16(kbase + 64 * i);
-    // V: rows of this block, 16-byte pieces in row-major order
+    // K and V: rows of this block, 16-byte pieces in row-major order
     constexpr int R = ROWB / 16;                 // lanes per row
     constexpr int RPI = 64 / R;                  // rows per load instruction
     constexpr int LPB = TR::VLOADS / 2;          // loads per lane per block
 #pragma unroll
     for (int i = 0; i < LPB; ++i) {
       const int rr = (lane / R) + RPI * i;       // row within the block (0..15)
-      r.v[blk * LPB + i] = ld16_stream(vp + (row + rr) * ROWB + (size_t)(lane % R) * 16);
+      const size_t off = (row + rr) * ROWB + (size_t)(lane % R) * 16;
+      r.k[blk * LPB + i] = ld16_stream(kp + off);
+      r.v[blk * LPB + i] = ld16_stream(vp + off);
     }
   }
 }
@@ -135,8 +128,10 @@ __global__ __launch_bounds__(256, 2) void decode_partial_mfma(AttnArgs a) {
   constexpr int ROWB = TR::VROWB;
   constexpr int R = ROWB / 16, RPI = 64 / R, LPB = TR::VLOADS / 2;
   constexpr int LDS_ROW = D * 2 + 32;           // bf16 V rows in LDS, padded against bank conflicts
+  constexpr int K_LDS_ROW = ROWB + 16;          // raw K rows in LDS (same slice, used before V)
   constexpr int STAGE_BYTES = kWaves * kTile * LDS_ROW;
-  constexpr int MERGE_BYTES = (kWaves * 16 * D + kWaves * 32) * 4;
+  constexpr int OROW = D + 4;                   // padded rows of the merge image (floats)
+  constexpr int MERGE_BYTES = (kWaves * 16 * OROW + kWaves * 32) * 4;
   __shared__ __attribute__((aligned(16)))
   uint8_t smem[STAGE_BYTES > MERGE_BYTES ? STAGE_BYTES : MERGE_BYTES];
 
@@ -187,66 +182,56 @@ __global__ __launch_bounds__(256, 2) void decode_partial_mfma(AttnArgs a) {
   uint8_t* lds = smem + w * kTile * LDS_ROW;
   constexpr int STRIDE = kWaves * kTile;
 
-  // Ping-pong pipeline over this wave's tiles t0, t0+STRIDE, ...: while a
-  // tile is computed the next one's loads are in flight, and the page ids of
-  // the tile after that are already in registers.
-  int t0 = t_begin + w * kTile;
-  TR bufA, bufB;
-  int pa0 = 0, pa1 = 0, pb0 = 0, pb1 = 0;
-  if (t0 < t_end) {
-    tile_pages(btrow, t0, t_end, pshift, pa0, pa1);
-    load_tile<KVT, D>(bufA, kp, vp, pa0, pa1, t0, t_end, Hkv, j, pshift, lane);
-    if (t0 + STRIDE < t_end) tile_pages(btrow, t0 + STRIDE, t_end, pshift, pb0, pb1);
-  }
-  auto step = [&](TR& cur, TR& nxt, int& q0, int& q1, const int& n0, const int& n1) {
-    // cur: tile t0 (loaded); nxt: receives tile t0+STRIDE (pages n0/n1);
-    // q0/q1 receive the pages of tile t0+2*STRIDE.
-    const int t1 = t0 + STRIDE;
-    if (t1 < t_end) {
-      load_tile<KVT, D>(nxt, kp, vp, n0, n1, t1, t_end, Hkv, j, pshift, lane);
-      if (t1 + STRIDE < t_end) tile_pages(btrow, t1 + STRIDE, t_end, pshift, q0, q1);
+  // Register ring over this wave's tiles t0, t0+STRIDE, ...: NB tile images,
+  // NB-1 of them in flight while one is computed (fp8 tiles are small, so the
+  // ring is deeper there); the page ids of the next tile to load are fetched
+  // one step before they are needed.
+  constexpr int NB = 2;
+  TR buf[NB];
+  int pn0 = 0, pn1 = 0;                         // pages of the next tile to load
+  int tl = t_begin + w * kTile;                 // next tile to load
+#pragma unroll
+  for (int s = 0; s < NB - 1; ++s) {
+    if (tl < t_end) {
+      tile_pages(btrow, tl, t_end, pshift, pn0, pn1);
+      load_tile<KVT, D>(buf[s], kp, vp, pn0, pn1, tl, t_end, Hkv, j, pshift, lane);
     }
+    tl += STRIDE;
+  }
+  if (tl < t_end) tile_pages(btrow, tl, t_end, pshift, pn0, pn1);
+
+  auto compute = [&](const TR& cur, const int t0) {
     const bool full = t0 + kTile <= t_end;
 
-    // ---- V rows -> LDS (row-major bf16), zeroing rows past the end ----
+    // ---- K rows -> LDS (raw storage format, padded rows) ----
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
+    for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
       for (int i = 0; i < LPB; ++i) {
-        const int rr = (lane / R) + RPI * i;
-        const int tok = 16 * blk + rr;
-        u32x4 x = cur.v[blk * LPB + i];
-        if (!full && t0 + tok >= t_end) x = u32x4{0, 0, 0, 0};
-        if constexpr (KVT == KV_FP8) {
-          u32x4 lo, hi;
-          fp8x16_to_bf16(x, lo, hi);
-          uint8_t* dst = lds + tok * LDS_ROW + (lane % R) * 32;
-          *reinterpret_cast<u32x4*>(dst) = lo;
-          *reinterpret_cast<u32x4*>(dst + 16) = hi;
-        } else {
-          *reinterpret_cast<u32x4*>(lds + tok * LDS_ROW + (lane % R) * 16) = x;
-        }
+        const int tok = 16 * blk + (lane / R) + RPI * i;
+        *reinterpret_cast<u32x4*>(lds + tok * K_LDS_ROW + (lane % R) * 16) = cur.k[blk * LPB + i];
       }
-    }
 
     // ---- S^T = K Q^T for the two 16-token blocks ----
+    // A operand of step kk, lane (g, n): token n, 16-byte piece 4*(kk / SPP) + g
+    // (SPP = MFMA steps per piece: 1 for bf16, 2 for fp8).
     f32x4 s[2];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       f32x4 acc = {0, 0, 0, 0};
+      const uint8_t* krow = lds + (16 * blk + h) * K_LDS_ROW + 16 * g4;
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         u32x4 ka;
         if constexpr (KVT == KV_FP8) {
-          // fp8: the lane's 32 codes are two u32x4; step kk uses codes 8kk..8kk+7
-          const u32x4& src = cur.k[blk][kk >> 1];
+          const u32x4 src = *reinterpret_cast<const u32x4*>(krow + 64 * (kk >> 1));
           const int o2 = (kk & 1) * 2;
           ka[0] = fp8x2_to_bf16x2<false>(src[o2]);
           ka[1] = fp8x2_to_bf16x2<true>(src[o2]);
           ka[2] = fp8x2_to_bf16x2<false>(src[o2 + 1]);
           ka[3] = fp8x2_to_bf16x2<true>(src[o2 + 1]);
         } else {
-          ka = cur.k[blk][kk];
+          ka = *reinterpret_cast<const u32x4*>(krow + 64 * kk);
         }
         acc = mfma16(ka, qb[kk], acc);
       }
@@ -288,6 +273,27 @@ __global__ __launch_bounds__(256, 2) void decode_partial_mfma(AttnArgs a) {
     pb[2] = pack_bf16x2(p[4], p[5]);
     pb[3] = pack_bf16x2(p[6], p[7]);
 
+    // ---- V rows -> LDS (row-major bf16), zeroing rows past the end ----
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+#pragma unroll
+      for (int i = 0; i < LPB; ++i) {
+        const int rr = (lane / R) + RPI * i;
+        const int tok = 16 * blk + rr;
+        u32x4 x = cur.v[blk * LPB + i];
+        if (!full && t0 + tok >= t_end) x = u32x4{0, 0, 0, 0};
+        if constexpr (KVT == KV_FP8) {
+          u32x4 lo, hi;
+          fp8x16_to_bf16(x, lo, hi);
+          uint8_t* dst = lds + tok * LDS_ROW + (lane % R) * 32;
+          *reinterpret_cast<u32x4*>(dst) = lo;
+          *reinterpret_cast<u32x4*>(dst + 16) = hi;
+        } else {
+          *reinterpret_cast<u32x4*>(lds + tok * LDS_ROW + (lane % R) * 16) = x;
+        }
+      }
+    }
+
     // ---- O^T += V^T P^T, V^T from the LDS image by transpose reads ----
     // lane (g, i) of a 16-lane group reads 4 bf16 of row 4g + i/4 (and 16 + ...)
     // at columns n0 + 4*(i%4); the hardware hands lane i column n0 + i.
@@ -307,12 +313,18 @@ __global__ __launch_bounds__(256, 2) void decode_partial_mfma(AttnArgs a) {
       o[dt] = mfma16(va, pb, o[dt]);
     }
   };
-  while (t0 < t_end) {
-    step(bufA, bufB, pa0, pa1, pb0, pb1);
-    t0 += STRIDE;
-    if (t0 >= t_end) break;
-    step(bufB, bufA, pb0, pb1, pa0, pa1);
-    t0 += STRIDE;
+  for (int base = t_begin + w * kTile; base < t_end; base += NB * STRIDE) {
+#pragma unroll
+    for (int s = 0; s < NB; ++s) {
+      const int tc = base + s * STRIDE;
+      if (tc >= t_end) break;
+      if (tl < t_end) {
+        load_tile<KVT, D>(buf[(s + NB - 1) % NB], kp, vp, pn0, pn1, tl, t_end, Hkv, j, pshift, lane);
+        if (tl + STRIDE < t_end) tile_pages(btrow, tl + STRIDE, t_end, pshift, pn0, pn1);
+      }
+      tl += STRIDE;
+      compute(buf[s], tc);
+    }
   }
 
   // ---- merge: 4 lanes per head within the wave (l is lane-partial) ----
@@ -321,12 +333,12 @@ __global__ __launch_bounds__(256, 2) void decode_partial_mfma(AttnArgs a) {
 
   // ---- merge the 4 waves through LDS ----
   __syncthreads();                               // all V slices consumed
-  float* sm_o = reinterpret_cast<float*>(smem);  // [kWaves][16][D]
-  float* sm_ml = sm_o + kWaves * 16 * D;         // [kWaves][16][2]
+  float* sm_o = reinterpret_cast<float*>(smem);  // [kWaves][16][OROW]
+  float* sm_ml = sm_o + kWaves * 16 * OROW;      // [kWaves][16][2]
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sm_o[(w * 16 + h) * D + 16 * dt + 4 * g4 + r] = o[dt][r];
+    for (int r = 0; r < 4; ++r) sm_o[(w * 16 + h) * OROW + 16 * dt + 4 * g4 + r] = o[dt][r];
   if (g4 == 0) { sm_ml[(w * 16 + h) * 2] = m; sm_ml[(w * 16 + h) * 2 + 1] = l; }
   __syncthreads();
   for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
@@ -340,7 +352,7 @@ __global__ __launch_bounds__(256, 2) void decode_partial_mfma(AttnArgs a) {
       const float mw = sm_ml[(ww * 16 + hh) * 2];
       const float f = (mw == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
       lt = fmaf(sm_ml[(ww * 16 + hh) * 2 + 1], f, lt);
-      at = fmaf(sm_o[(ww * 16 + hh) * D + d], f, at);
+      at = fmaf(sm_o[(ww * 16 + hh) * OROW + d], f, at);
     }
     const int hq = j * G + hh;
     if (n_split == 1) {
