@@ -327,7 +327,10 @@ __global__ __launch_bounds__(256) void decode_partial_vec(AttnArgs a) {
   }
 }
 
-// Merge: one wave per (row, query head); lanes cover head_dim.
+// Merge: one wave per (row, query head).  Lanes first take one context range
+// each (the (m, l) pairs: max and weighted sum by wave reductions), then
+// cover head_dim and sum the weighted accumulators, four ranges per batch of
+// independent loads.
 template <typename OT, int D>
 __global__ __launch_bounds__(256) void lse_merge_kernel(AttnArgs a) {
   const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -340,17 +343,40 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(AttnArgs a) {
   if (n <= 1) return;
   const size_t base = ((size_t)z * Hq + h) * a.max_splits;
   float M = -INFINITY;
-  for (int s = 0; s < n; ++s) M = fmaxf(M, a.ws_ml[(base + s) * 2]);
+  for (int s0 = 0; s0 < n; s0 += 64)
+    if (s0 + lane < n) M = fmaxf(M, a.ws_ml[(base + s0 + lane) * 2]);
+#pragma unroll
+  for (int msk = 32; msk >= 1; msk >>= 1) M = fmaxf(M, __shfl_xor(M, msk, 64));
   float den = 0.0f;
+  for (int s0 = 0; s0 < n; s0 += 64)
+    if (s0 + lane < n) {
+      const float m_s = a.ws_ml[(base + s0 + lane) * 2], l_s = a.ws_ml[(base + s0 + lane) * 2 + 1];
+      den = fmaf(l_s, __builtin_amdgcn_exp2f(m_s - M), den);
+    }
+#pragma unroll
+  for (int msk = 32; msk >= 1; msk >>= 1) den += __shfl_xor(den, msk, 64);
   constexpr int PER = D / 64;
   float o[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) o[k] = 0.0f;
-  for (int s = 0; s < n; ++s) {
-    const float f = __builtin_amdgcn_exp2f(a.ws_ml[(base + s) * 2] - M);
-    den = fmaf(a.ws_ml[(base + s) * 2 + 1], f, den);
+  for (int s0 = 0; s0 < n; s0 += 64) {
+    // weight of range s0 + lane, broadcast below by shuffles
+    const float wl = (s0 + lane < n) ? __builtin_amdgcn_exp2f(a.ws_ml[(base + s0 + lane) * 2] - M) : 0.0f;
+    const int cnt = min(64, n - s0);
+    for (int s = 0; s < cnt; s += 4) {
+      float acc[4][PER], wv[4];
 #pragma unroll
-    for (int k = 0; k < PER; ++k) o[k] = fmaf(a.ws_acc[(base + s) * D + lane + 64 * k], f, o[k]);
+      for (int u = 0; u < 4; ++u) {
+        const int ss = min(s + u, cnt - 1);      // clamped duplicates get weight 0
+        wv[u] = (s + u < cnt) ? __shfl(wl, ss, 64) : 0.0f;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) acc[u][k] = a.ws_acc[(base + s0 + ss) * D + lane + 64 * k];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int k = 0; k < PER; ++k) o[k] = fmaf(acc[u][k], wv[u], o[k]);
+    }
   }
   const float inv = 1.0f / den;
 #pragma unroll
