@@ -45,6 +45,7 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kTile = 32;                      // tokens per wave tile
+constexpr int kMaxRangePages = 512;            // block-table entries staged per work item
 
 typedef __bf16 bf16x8_t __attribute__((__vector_size__(16)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -78,11 +79,13 @@ struct TileRegs {
 };
 
 // Page ids of the two 16-token blocks of the tile at t0 (a block past the end
-// reuses the first block's page: in bounds, and masked later).
-__device__ __forceinline__ void tile_pages(const int32_t* btrow, int t0, int t_end, int pshift,
-                                           int& p0, int& p1) {
-  p0 = btrow[t0 >> pshift];
-  p1 = (t0 + 16 < t_end) ? btrow[(t0 + 16) >> pshift] : p0;
+// reuses the first block's page: in bounds, and masked later).  `pages` holds
+// the block-table entries of this work item's range, from entry `first`.
+__device__ __forceinline__ void tile_pages(const int32_t* pages,
+                                           int first, int t0, int t_end,
+                                           int pshift, int& p0, int& p1) {
+  p0 = pages[(t0 >> pshift) - first];
+  p1 = (t0 + 16 < t_end) ? pages[((t0 + 16) >> pshift) - first] : p0;
 }
 
 // First of the 8 consecutive d values that MFMA step kk takes for lane group g:
@@ -170,6 +173,8 @@ __global__ __launch_bounds__(256, 2) void decode_partial_mfma(AttnArgs a) {
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) qb[kk] = ld16(q + k_elem_offset<KVT>(kk, g4));
   }
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) settle(qb[kk]);
 
   f32x4 o[DT];
 #pragma unroll
@@ -177,28 +182,35 @@ __global__ __launch_bounds__(256, 2) void decode_partial_mfma(AttnArgs a) {
   float m = -INFINITY, l = 0.0f;
 
   const int32_t* btrow = a.bt + (size_t)z * a.bt_stride;
+  // The range's block-table entries, staged in LDS once: page lookups then
+  // never wait behind the K/V loads in flight (vector-memory waits retire in
+  // order).  The host routes ranges of more than kMaxRangePages pages to the
+  // vector path.
+  __shared__ int32_t pages[kMaxRangePages];
+  const int first = t_begin >> pshift;
+  const int npg = ((t_end - 1) >> pshift) - first + 1;
+  for (int i = threadIdx.x; i < npg; i += blockDim.x) pages[i] = btrow[first + i];
+  __syncthreads();
   const uint8_t* kp = static_cast<const uint8_t*>(a.c.k_pool);
   const uint8_t* vp = static_cast<const uint8_t*>(a.c.v_pool);
   uint8_t* lds = smem + w * kTile * LDS_ROW;
   constexpr int STRIDE = kWaves * kTile;
 
-  // Register ring over this wave's tiles t0, t0+STRIDE, ...: NB tile images,
-  // NB-1 of them in flight while one is computed (fp8 tiles are small, so the
-  // ring is deeper there); the page ids of the next tile to load are fetched
-  // one step before they are needed.
-  constexpr int NB = 2;
-  TR buf[NB];
+  // This wave's tiles are t_begin + w*kTile + k*STRIDE, k = 0..nt-1.  Two
+  // register images alternate: while one tile is computed the next one's
+  // loads are in flight, and the page ids of the tile after that are read
+  // from LDS.  The main loop only runs while a next tile exists, so every
+  // load in it is unconditional and the wait for the current tile's data
+  // never has to cover the next tile's loads; the last tiles are peeled.
+  const int tw0 = t_begin + w * kTile;
+  const int nt = tw0 < t_end ? (t_end - tw0 + STRIDE - 1) / STRIDE : 0;
+  TR buf0, buf1;
   int pn0 = 0, pn1 = 0;                         // pages of the next tile to load
-  int tl = t_begin + w * kTile;                 // next tile to load
-#pragma unroll
-  for (int s = 0; s < NB - 1; ++s) {
-    if (tl < t_end) {
-      tile_pages(btrow, tl, t_end, pshift, pn0, pn1);
-      load_tile<KVT, D>(buf[s], kp, vp, pn0, pn1, tl, t_end, Hkv, j, pshift, lane);
-    }
-    tl += STRIDE;
+  if (nt > 0) {
+    tile_pages(pages, first, tw0, t_end, pshift, pn0, pn1);
+    load_tile<KVT, D>(buf0, kp, vp, pn0, pn1, tw0, t_end, Hkv, j, pshift, lane);
+    if (nt > 1) tile_pages(pages, first, tw0 + STRIDE, t_end, pshift, pn0, pn1);
   }
-  if (tl < t_end) tile_pages(btrow, tl, t_end, pshift, pn0, pn1);
 
   auto compute = [&](const TR& cur, const int t0) {
     const bool full = t0 + kTile <= t_end;
@@ -313,18 +325,24 @@ __global__ __launch_bounds__(256, 2) void decode_partial_mfma(AttnArgs a) {
       o[dt] = mfma16(va, pb, o[dt]);
     }
   };
-  for (int base = t_begin + w * kTile; base < t_end; base += NB * STRIDE) {
-#pragma unroll
-    for (int s = 0; s < NB; ++s) {
-      const int tc = base + s * STRIDE;
-      if (tc >= t_end) break;
-      if (tl < t_end) {
-        load_tile<KVT, D>(buf[(s + NB - 1) % NB], kp, vp, pn0, pn1, tl, t_end, Hkv, j, pshift, lane);
-        if (tl + STRIDE < t_end) tile_pages(btrow, tl + STRIDE, t_end, pshift, pn0, pn1);
-      }
-      tl += STRIDE;
-      compute(buf[s], tc);
-    }
+  // step(k, cur, nxt): load tile k+1 into nxt (its pages are pn0/pn1), read
+  // the pages of tile k+2, compute tile k from cur.
+  auto step = [&](int k, const TR& cur, TR& nxt) {
+    const int tn = tw0 + (k + 1) * STRIDE;
+    load_tile<KVT, D>(nxt, kp, vp, pn0, pn1, tn, t_end, Hkv, j, pshift, lane);
+    if (k + 2 < nt) tile_pages(pages, first, tn + STRIDE, t_end, pshift, pn0, pn1);
+    compute(cur, tw0 + k * STRIDE);
+  };
+  int k = 0;
+  for (; k + 2 < nt; k += 2) {
+    step(k, buf0, buf1);
+    step(k + 1, buf1, buf0);
+  }
+  if (k + 1 < nt) {                              // two tiles left: buf0 holds tile k
+    step(k, buf0, buf1);
+    compute(buf1, tw0 + (k + 1) * STRIDE);
+  } else if (k < nt) {                           // one tile left
+    compute(buf0, tw0 + k * STRIDE);
   }
 
   // ---- merge: 4 lanes per head within the wave (l is lane-partial) ----
@@ -371,7 +389,8 @@ __global__ __launch_bounds__(256, 2) void decode_partial_mfma(AttnArgs a) {
 bool decode_mfma_supported(const AttnArgs& a) {
   const int G = a.num_q_heads / a.c.num_kv_heads;
   return !a.prefill && G >= 3 && G <= 16 && a.c.kv_dtype != KV_F32 &&
-         (a.c.head_dim == 64 || a.c.head_dim == 128);
+         (a.c.head_dim == 64 || a.c.head_dim == 128) &&
+         (a.split_tokens >> a.page_shift) + 2 <= kMaxRangePages;
 }
 
 hipError_t launch_decode_partial_mfma(const AttnArgs& a, hipStream_t s) {

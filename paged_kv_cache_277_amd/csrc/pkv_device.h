@@ -135,6 +135,13 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// Marks a loaded register as consumed here.  Registers that are loaded before
+// a loop and only read inside it (MFMA operands held for the whole loop) would
+// otherwise be treated as possibly in flight at every iteration, and since
+// vector-memory counters retire in order, each wait for them would also wait
+// for the prefetch loads issued in that iteration.
+__device__ __forceinline__ void settle(const u32x4& x) { asm volatile("" ::"v"(x)); }
+
 // Wave-uniform copy of a value (lets the compiler keep it in an SGPR).
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 

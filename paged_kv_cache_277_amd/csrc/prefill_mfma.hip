@@ -8,11 +8,11 @@
 // "TensorRT-LLM性能调优：提升LLM推理效率"; running max / sum, §6.1).
 //
 // Work decomposition (MI355X): the G query heads that share KV head j, times
-// the chunk's tokens, form "rows" (row = token*G + head).  A workgroup owns 64
-// consecutive rows of one (request, KV head) — 16 per wave, one MFMA N-tile —
-// and walks the keys 0 .. (its last row's position) in 32-token tiles.  Each
+// the chunk's tokens, form "rows" (row = token*G + head).  A workgroup owns 128
+// consecutive rows of one (request, KV head) — 32 per wave, two MFMA N-tiles
+// that share every K and V^T operand read from LDS — and walks the keys 0 .. (its last row's position) in 32-token tiles.  Each
 // K/V tile is fetched from the pages once per workgroup into LDS and shared by
-// the four waves; loads run two tiles ahead of the compute (register
+// the four waves; loads run three tiles ahead of the compute (register
 // staging, double-buffered LDS), with the request's block-table entries
 // staged in LDS so no load waits on another:
 //
@@ -35,7 +35,8 @@ namespace pkv {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kRows = 16 * kWaves;          // rows per workgroup
+constexpr int kNt = 2;                      // 16-row MFMA N-tiles per wave
+constexpr int kRows = 16 * kNt * kWaves;    // rows per workgroup
 constexpr int kTile = 32;                   // keys per tile
 constexpr int kMaxPages = 512;              // block-table entries staged per workgroup
 
@@ -72,6 +73,9 @@ template <int KVT, int D>
 __device__ __forceinline__ void pf_load(PfRegs<KVT, D>& r, const uint8_t* kp, const uint8_t* vp,
                                         const int32_t* pages, int t0, int kmax, int Hkv, int j,
                                         int pshift) {
+  // Every call issues the same loads: pieces past kmax (or past the tile)
+  // read the first 16 bytes of the pools instead, and pf_store zeroes them.
+  // A fixed load count keeps the waits for older tiles exact.
   using S = PfShape<KVT, D>;
   constexpr int PR = S::ROWB / 16;                          // pieces per row
   const int pmask = (1 << pshift) - 1;
@@ -80,24 +84,33 @@ __device__ __forceinline__ void pf_load(PfRegs<KVT, D>& r, const uint8_t* kp, co
     const int piece = threadIdx.x + 256 * i;
     const int tok = piece / PR, pc = piece % PR;
     const int t = t0 + tok;
-    if (piece < S::PIECES && t < kmax) {
-      const int page = pages[t >> pshift];
-      const size_t off = ((((size_t)page * Hkv + j) << pshift | (size_t)(t & pmask)) * S::ROWB) +
-                         (size_t)pc * 16;
-      r.k[i] = ld16(kp + off);
-      r.v[i] = ld16(vp + off);
-    } else {
-      r.k[i] = u32x4{0, 0, 0, 0};
-      r.v[i] = u32x4{0, 0, 0, 0};
-    }
+    const bool ok = piece < S::PIECES && t < kmax;
+    const int page = ok ? pages[t >> pshift] : 0;
+    const size_t off = ok ? ((((size_t)page * Hkv + j) << pshift | (size_t)(t & pmask)) * S::ROWB) +
+                                (size_t)pc * 16
+                          : 0;
+    r.k[i] = ld16(kp + off);
+    r.v[i] = ld16(vp + off);
   }
 }
 
-// Registers -> LDS (bf16 rows, padded).
+// Registers -> LDS (bf16 rows, padded); rows at or past kmax become zeros
+// (masked keys must carry finite values: their probability is exactly 0).
 template <int KVT, int D>
-__device__ __forceinline__ void pf_store(const PfRegs<KVT, D>& r, uint8_t* kl, uint8_t* vl) {
+__device__ __forceinline__ void pf_store(PfRegs<KVT, D> r, uint8_t* kl, uint8_t* vl, int t0,
+                                         int kmax) {
   using S = PfShape<KVT, D>;
   constexpr int PR = S::ROWB / 16;
+  if (t0 + kTile > kmax) {                       // last tile of the range only
+#pragma unroll
+    for (int i = 0; i < S::PPT; ++i) {
+      const int piece = threadIdx.x + 256 * i;
+      if (t0 + piece / PR >= kmax) {
+        r.k[i] = u32x4{0, 0, 0, 0};
+        r.v[i] = u32x4{0, 0, 0, 0};
+      }
+    }
+  }
 #pragma unroll
   for (int i = 0; i < S::PPT; ++i) {
     const int piece = threadIdx.x + 256 * i;
@@ -153,33 +166,48 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma(AttnArgs a, int nqb) {
   const int lane = threadIdx.x & 63;
   const int w = uniform(threadIdx.x >> 6);
   const int g4 = lane >> 4, n = lane & 15;
-  const int my_row = row0 + 16 * w + n;          // this lane's row in S^T / O^T column n
-  const bool row_ok = my_row < C * G;
-  const int my_tok = my_row / G, my_head = my_row - my_tok * G;
-  const int my_lim = Pr + my_tok;                // last key this row may see
-  const int wave_last = min(C * G, row0 + 16 * w + 16) - 1;   // last real row of this wave
-  const int wave_kmax = wave_last >= row0 + 16 * w ? Pr + wave_last / G + 1 : 0;
-  const int wave_min_lim = Pr + (row0 + 16 * w) / G;           // smallest key limit in the wave
+  const int wrow0 = row0 + kNt * 16 * w;         // first row of this wave
+  const int wave_last = min(C * G, wrow0 + kNt * 16) - 1;    // last real row of this wave
+  const int wave_kmax = wave_last >= wrow0 ? Pr + wave_last / G + 1 : 0;
+  const int wave_min_lim = Pr + wrow0 / G;       // smallest key limit in the wave
 
   float kscale = 1.0f, vscale = 1.0f;
   if constexpr (KVT == KV_FP8) { kscale = a.c.k_scale[j]; vscale = a.c.v_scale[j]; }
   const float smul = a.sm_scale * kLog2e * kscale;
 
-  // Q^T (B operand): lane (g4, n) holds Q[row n][g4*D/4 + 8kk + e].
-  u32x4 qb_reg[KK];
+  // Per N-tile nt: this lane's row (column n of S^T / O^T) and its Q^T
+  // B operand: lane (g4, n) holds Q[row][g4*D/4 + 8kk + e].
+  int my_lim[kNt];
+  bool row_ok[kNt];
+  size_t row_off[kNt];
+  u32x4 qb_reg[kNt][KK];
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) qb_reg[kk] = u32x4{0, 0, 0, 0};
-  if (row_ok) {
-    const uint16_t* q = static_cast<const uint16_t*>(a.q) +
-                        ((size_t)(c0 + my_tok) * Hq + (size_t)j * G + my_head) * D;
+  for (int nt = 0; nt < kNt; ++nt) {
+    const int my_row = wrow0 + 16 * nt + n;
+    row_ok[nt] = my_row < C * G;
+    const int my_tok = my_row / G, my_head = my_row - my_tok * G;
+    my_lim[nt] = Pr + my_tok;
+    row_off[nt] = ((size_t)(c0 + my_tok) * Hq + (size_t)j * G + my_head) * D;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) qb_reg[kk] = ld16(q + (D / 4) * g4 + 8 * kk);
+    for (int kk = 0; kk < KK; ++kk) qb_reg[nt][kk] = u32x4{0, 0, 0, 0};
+    if (row_ok[nt]) {
+      const uint16_t* q = static_cast<const uint16_t*>(a.q) + row_off[nt];
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) qb_reg[nt][kk] = ld16(q + (D / 4) * g4 + 8 * kk);
+    }
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) settle(qb_reg[nt][kk]);
   }
 
-  f32x4 o[DT];
+  f32x4 o[kNt][DT];
+  float m[kNt], l[kNt];
 #pragma unroll
-  for (int i = 0; i < DT; ++i) o[i] = f32x4{0, 0, 0, 0};
-  float m = -INFINITY, l = 0.0f;
+  for (int nt = 0; nt < kNt; ++nt) {
+#pragma unroll
+    for (int i = 0; i < DT; ++i) o[nt][i] = f32x4{0, 0, 0, 0};
+    m[nt] = -INFINITY;
+    l[nt] = 0.0f;
+  }
 
   const int32_t* btrow = a.bt + (size_t)r * a.bt_stride;
   const uint8_t* kp = static_cast<const uint8_t*>(a.c.k_pool);
@@ -193,76 +221,82 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma(AttnArgs a, int nqb) {
   for (int i = threadIdx.x; i < npages; i += blockDim.x) pages[i] = btrow[i];
   __syncthreads();
 
-  // Pipeline: tile t is staged in register set t % 2 and LDS buffer t % 2.
-  // While tile i is computed, the loads of tile i+2 are in flight and tile
-  // i+1 (loaded one step earlier) is written to the other LDS buffer.
-  PfRegs<KVT, D> r0, r1;
+  // Pipeline: tile t is staged in register set t % 3 and LDS buffer t % 2.
+  // While tile i is computed, the loads of tiles i+2 and i+3 are in flight
+  // and tile i+1 (loaded two steps earlier) is written to the other LDS
+  // buffer, so each load has two compute steps to land.
+  PfRegs<KVT, D> r0, r1, r2;
   pf_load<KVT, D>(r0, kp, vp, pages, 0, kmax, Hkv, j, pshift);
-  if (ntiles > 1) pf_load<KVT, D>(r1, kp, vp, pages, kTile, kmax, Hkv, j, pshift);
-  pf_store<KVT, D>(r0, smem, smem + kTile * S::K_LDS);
+  pf_load<KVT, D>(r1, kp, vp, pages, kTile, kmax, Hkv, j, pshift);
+  pf_load<KVT, D>(r2, kp, vp, pages, 2 * kTile, kmax, Hkv, j, pshift);
+  pf_store<KVT, D>(r0, smem, smem + kTile * S::K_LDS, 0, kmax);
   __syncthreads();
 
   auto step = [&](int it, PfRegs<KVT, D>& rfree, const PfRegs<KVT, D>& rnext) {
     const int t0 = it * kTile;
     uint8_t* kl = smem + (it & 1) * S::STAGE;
     uint8_t* vl = kl + kTile * S::K_LDS;
-    if (it + 2 < ntiles) pf_load<KVT, D>(rfree, kp, vp, pages, t0 + 2 * kTile, kmax, Hkv, j, pshift);
+    pf_load<KVT, D>(rfree, kp, vp, pages, t0 + 3 * kTile, kmax, Hkv, j, pshift);
 
     if (t0 < wave_kmax) {                        // skip tiles wholly above this wave's diagonal
-      // ---- S^T for the two 16-key blocks ----
-      f32x4 s[2];
+      // ---- S^T for the two 16-key blocks; each K operand feeds every N-tile ----
+      f32x4 s[kNt][2];
+#pragma unroll
+      for (int nt = 0; nt < kNt; ++nt) s[nt][0] = s[nt][1] = f32x4{0, 0, 0, 0};
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
-        f32x4 acc = {0, 0, 0, 0};
         const uint8_t* krow = kl + (16 * blk + n) * S::K_LDS + g4 * (D / 4) * 2;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
           const u32x4 ka = *reinterpret_cast<const u32x4*>(krow + 16 * kk);
-          acc = mfma16(ka, qb_reg[kk], acc);
+#pragma unroll
+          for (int nt = 0; nt < kNt; ++nt) s[nt][blk] = mfma16(ka, qb_reg[nt][kk], s[nt][blk]);
         }
-        s[blk] = acc;
       }
-      // Raw scores; the causal mask only matters on tiles that cross this
-      // wave's diagonal.  The scale enters the exponent as one FMA.
-      float sv[8];
+      // ---- online softmax per N-tile; the scale enters the exponent as one FMA ----
+      const bool diag = t0 + kTile - 1 > wave_min_lim;
+      u32x4 pb[kNt];
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) sv[4 * blk + rr] = s[blk][rr];
-      if (t0 + kTile - 1 > wave_min_lim) {
+      for (int nt = 0; nt < kNt; ++nt) {
+        float sv[8];
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr)
-            if (t0 + 16 * blk + 4 * g4 + rr > my_lim) sv[4 * blk + rr] = -INFINITY;
-      }
-      float mx = sv[0];
+          for (int rr = 0; rr < 4; ++rr) sv[4 * blk + rr] = s[nt][blk][rr];
+        if (diag) {
 #pragma unroll
-      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      // Key 0 is visible to every row (padding rows included), so mx is
-      // finite on the first tile and m stays finite afterwards.
-      const float mn = fmaxf(m, mx * smul);
-      if (__any(mn > m)) {                       // rescale only when some row's max grew
-        const float alpha = __builtin_amdgcn_exp2f(m - mn);
-        l *= alpha;
+          for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-        for (int i = 0; i < DT; ++i) o[i] *= alpha;
-        m = mn;
-      }
-      float p[8];
+            for (int rr = 0; rr < 4; ++rr)
+              if (t0 + 16 * blk + 4 * g4 + rr > my_lim[nt]) sv[4 * blk + rr] = -INFINITY;
+        }
+        float mx = sv[0];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        p[i] = __builtin_amdgcn_exp2f(fmaf(sv[i], smul, -m));
-        l += p[i];
+        for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        // Key 0 is visible to every row (padding rows included), so mx is
+        // finite on the first tile and m stays finite afterwards.
+        const float mn = fmaxf(m[nt], mx * smul);
+        if (__any(mn > m[nt])) {                 // rescale only when some row's max grew
+          const float alpha = __builtin_amdgcn_exp2f(m[nt] - mn);
+          l[nt] *= alpha;
+#pragma unroll
+          for (int i = 0; i < DT; ++i) o[nt][i] *= alpha;
+          m[nt] = mn;
+        }
+        float p[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          p[i] = __builtin_amdgcn_exp2f(fmaf(sv[i], smul, -m[nt]));
+          l[nt] += p[i];
+        }
+        pb[nt][0] = pack_bf16x2(p[0], p[1]);
+        pb[nt][1] = pack_bf16x2(p[2], p[3]);
+        pb[nt][2] = pack_bf16x2(p[4], p[5]);
+        pb[nt][3] = pack_bf16x2(p[6], p[7]);
       }
-      u32x4 pb;
-      pb[0] = pack_bf16x2(p[0], p[1]);
-      pb[1] = pack_bf16x2(p[2], p[3]);
-      pb[2] = pack_bf16x2(p[4], p[5]);
-      pb[3] = pack_bf16x2(p[6], p[7]);
-      // ---- O^T += V^T P^T ----
+      // ---- O^T += V^T P^T; each V^T operand feeds every N-tile ----
       const int rd_row0 = 4 * g4 + (n >> 2);
       const int rd_col = 4 * (n & 3);
       typedef s16x4 __attribute__((address_space(3))) * lds_s16x4_ptr;
@@ -275,36 +309,40 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma(AttnArgs a, int nqb) {
         s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(vbase + off1));
         u32x2 w0 = __builtin_bit_cast(u32x2, v0), w1 = __builtin_bit_cast(u32x2, v1);
         const u32x4 va = {w0[0], w0[1], w1[0], w1[1]};
-        o[dt] = mfma16(va, pb, o[dt]);
+#pragma unroll
+        for (int nt = 0; nt < kNt; ++nt) o[nt][dt] = mfma16(va, pb[nt], o[nt][dt]);
       }
     }
     if (it + 1 < ntiles) {
       uint8_t* kn = smem + ((it + 1) & 1) * S::STAGE;
-      pf_store<KVT, D>(rnext, kn, kn + kTile * S::K_LDS);
+      pf_store<KVT, D>(rnext, kn, kn + kTile * S::K_LDS, t0 + kTile, kmax);
     }
     __syncthreads();
   };
 
-  for (int it = 0; it < ntiles; it += 2) {
+  for (int it = 0; it < ntiles; it += 3) {
     step(it, r0, r1);
-    if (it + 1 < ntiles) step(it + 1, r1, r0);
+    if (it + 1 < ntiles) step(it + 1, r1, r2);
+    if (it + 2 < ntiles) step(it + 2, r2, r0);
   }
 
   // ---- finish rows: l is split over the 4 lanes of a row ----
-  l += __shfl_xor(l, 16, 64);
-  l += __shfl_xor(l, 32, 64);
-  if (row_ok) {
-    const float inv = vscale / l;
-    uint16_t* out = static_cast<uint16_t*>(a.out) +
-                    ((size_t)(c0 + my_tok) * Hq + (size_t)j * G + my_head) * D;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const uint32_t lo = pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv);
-      const uint32_t hi = pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv);
-      *reinterpret_cast<u32x2*>(out + 16 * dt + 4 * g4) = u32x2{lo, hi};
+  for (int nt = 0; nt < kNt; ++nt) {
+    float lt = l[nt];
+    lt += __shfl_xor(lt, 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
+    if (row_ok[nt]) {
+      const float inv = vscale / lt;
+      uint16_t* out = static_cast<uint16_t*>(a.out) + row_off[nt];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const uint32_t lo = pack_bf16x2(o[nt][dt][0] * inv, o[nt][dt][1] * inv);
+        const uint32_t hi = pack_bf16x2(o[nt][dt][2] * inv, o[nt][dt][3] * inv);
+        *reinterpret_cast<u32x2*>(out + 16 * dt + 4 * g4) = u32x2{lo, hi};
+      }
+      if (g4 == 0 && a.lse) a.lse[row_off[nt] / D] = (m[nt] + __log2f(lt)) * kLn2;
     }
-    if (g4 == 0 && a.lse)
-      a.lse[(size_t)(c0 + my_tok) * Hq + (size_t)j * G + my_head] = (m + __log2f(l)) * kLn2;
   }
 }
 
