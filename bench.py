@@ -131,6 +131,8 @@ def main() -> int:
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of the step captured as one HIP graph")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain device copy of known size instead (counter scaling)")
     args = ap.parse_args()
@@ -167,9 +169,13 @@ def main() -> int:
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(K)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    graph = dw.capture_step() if args.graph else None
     torch.cuda.synchronize()
     start.record()
     for i in range(K):
+        if graph is not None:
+            graph.replay()
+            continue
         dw.append_step()
         if wl.num_seqs:
             ev[i][0].record()
@@ -180,6 +186,18 @@ def main() -> int:
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / K
+    if graph is not None:
+        # The kernel's own duration cannot be bracketed inside a replay: time
+        # it in a short eager loop after the replays.
+        for i in range(K):
+            dw.append_step()
+            if wl.num_seqs:
+                ev[i][0].record()
+                dw.decode_partial()
+                ev[i][1].record()
+                dw.merge()
+            dw.prefill()
+        torch.cuda.synchronize()
     part_ms = float(np.mean([a.elapsed_time(b) for a, b in ev])) if wl.num_seqs else 0.0
 
     dec_bytes = wk.decode_bytes(spec, wl.context_lens) if wl.num_seqs else 0
@@ -211,7 +229,10 @@ def main() -> int:
                    "num_q_heads": spec.num_q_heads, "num_kv_heads": spec.num_kv_heads,
                    "head_dim": spec.head_dim, "page_size": spec.page_size,
                    "context_tokens": int(wl.context_lens.sum()),
-                   "split_tokens": dw.split_tokens, "parallelism": "single GPU"},
+                   "split_tokens": dw.split_tokens,
+                   "prefill_split_tokens": dw.pf["split"] if dw.pf else None,
+                   "parallelism": "single GPU",
+                   "launch": "hip graph replay" if args.graph else "eager launches"},
         "seq_steps_per_s": round(wl.num_seqs / (ms * 1e-3), 1),
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "step_bytes": step_bytes,

@@ -235,13 +235,25 @@ pkv_status pkv_lse_merge(const pkv_cache_desc* cache, void* out, int32_t out_dty
  * in the pages (pkv_kv_cache_append).  Row i of request r (absolute position
  * ctx_before[r] + i) attends keys 0 .. ctx_before[r] + i inclusive.
  *
- * q, out     : device packed [num_q_tokens][num_q_heads][head_dim]
- * lse        : device float[num_q_tokens][num_q_heads] or NULL
- * cu_q_lens  : device int32[num_reqs+1], chunk row offsets, cu[0] = 0,
- *              every chunk length <= max_chunk_len, cu[num_reqs] = num_q_tokens
- * ctx_before : device int32[num_reqs], tokens cached before the chunk;
- *              ctx_before[r] + chunk_len(r) <= bt_stride * page_size
- * Supported dtypes as for decode.  No workspace.
+ * As in decode, the keys are cut into ranges of split_tokens; a row whose
+ * keys span several ranges gets per-range partials in the workspace and the
+ * same log-sum-exp merge (launched by this call on the same stream).  Long
+ * contexts so spread over many workgroups instead of one long serial walk.
+ *
+ * q, out        : device packed [num_q_tokens][num_q_heads][head_dim]
+ * lse           : device float[num_q_tokens][num_q_heads] or NULL
+ * cu_q_lens     : device int32[num_reqs+1], chunk row offsets, cu[0] = 0,
+ *                 every chunk length <= max_chunk_len, cu[num_reqs] = num_q_tokens
+ * ctx_before    : device int32[num_reqs], tokens cached before the chunk;
+ *                 ctx_before[r] + chunk_len(r) <= max_total_len
+ * max_total_len : host bound on ctx_before[r] + chunk_len(r) over the batch,
+ *                 max_chunk_len <= max_total_len <= bt_stride * page_size
+ * split_tokens  : key range per work item, a positive multiple of 64; 0
+ *                 selects pkv_prefill_split_tokens().  F32 caches take one
+ *                 range only (split_tokens >= max_total_len, or 0).
+ * workspace     : device scratch of at least pkv_prefill_workspace_bytes(...)
+ *                 bytes (NULL when that is 0); contents on entry are ignored.
+ * Supported dtypes as for decode.
  * ------------------------------------------------------------------------ */
 pkv_status pkv_paged_attn_chunked_prefill(const pkv_cache_desc* cache,
                                           const void* q, int32_t q_dtype,
@@ -250,7 +262,23 @@ pkv_status pkv_paged_attn_chunked_prefill(const pkv_cache_desc* cache,
                                           const int32_t* block_tables, int32_t bt_stride,
                                           int32_t num_reqs, int32_t num_q_tokens,
                                           int32_t num_q_heads, int32_t max_chunk_len,
-                                          float sm_scale, void* stream);
+                                          int32_t max_total_len, float sm_scale,
+                                          int32_t split_tokens, void* workspace,
+                                          size_t workspace_bytes, void* stream);
+
+/* Default key range for a prefill batch (a multiple of 64; at least
+ * max_total_len, i.e. one range, for F32 caches).  Pure host function;
+ * returns 0 on invalid arguments. */
+int32_t pkv_prefill_split_tokens(const pkv_cache_desc* cache, int32_t num_reqs,
+                                 int32_t num_q_heads, int32_t max_chunk_len,
+                                 int32_t max_total_len);
+
+/* Workspace bytes a prefill call with these arguments needs (split_tokens
+ * resolved as in pkv_paged_attn_chunked_prefill; 0 for one range). */
+size_t pkv_prefill_workspace_bytes(const pkv_cache_desc* cache, int32_t num_reqs,
+                                   int32_t num_q_tokens, int32_t num_q_heads,
+                                   int32_t max_chunk_len, int32_t max_total_len,
+                                   int32_t split_tokens);
 
 /* ------------------------------------------------------------------------ *
  * Utilities

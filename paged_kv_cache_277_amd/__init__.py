@@ -9,4 +9,5 @@ from .binding import (PagedCache, PageAllocator, PkvError, decode_workspace, lib
                       pkv_decode_split_tokens, pkv_decode_workspace_bytes, pkv_fp8_e4m3fn_to_f32,
                       pkv_kv_cache_append, pkv_lse_merge, pkv_paged_attn_chunked_prefill,
                       pkv_paged_attn_decode, pkv_paged_attn_decode_partial,
+                      pkv_prefill_split_tokens, pkv_prefill_workspace_bytes, prefill_workspace,
                       pkv_validate_block_tables)

@@ -63,7 +63,10 @@ _SIGS = {
     "pkv_paged_attn_decode": (_I, [_P, _P, _I, _P, _I, _P, _P, _I, _P, _I, _I, _I, _F, _I, _P, _SZ, _P]),
     "pkv_paged_attn_decode_partial": (_I, [_P, _P, _I, _P, _I, _P, _P, _I, _P, _I, _I, _I, _F, _I, _P, _SZ, _P]),
     "pkv_lse_merge": (_I, [_P, _P, _I, _P, _P, _I, _I, _I, _I, _P, _SZ, _P]),
-    "pkv_paged_attn_chunked_prefill": (_I, [_P, _P, _I, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
+    "pkv_paged_attn_chunked_prefill": (_I, [_P, _P, _I, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I,
+                                            _I, _I, _F, _I, _P, _SZ, _P]),
+    "pkv_prefill_split_tokens": (_I, [_P, _I, _I, _I, _I]),
+    "pkv_prefill_workspace_bytes": (_SZ, [_P, _I, _I, _I, _I, _I, _I]),
     "pkv_validate_block_tables": (_I, [_P, _P, _I, _P, _I, _P]),
     "pkv_fp8_e4m3fn_to_f32": (_I, [_P, _P, C.c_int64, _P]),
 }
@@ -302,12 +305,39 @@ def pkv_lse_merge(cache: PagedCache, out: torch.Tensor, context_lens: torch.Tens
                                _stream(stream)))
 
 
+def pkv_prefill_split_tokens(cache: PagedCache, num_reqs: int, num_q_heads: int,
+                             max_chunk_len: int, max_total_len: int) -> int:
+    return lib().pkv_prefill_split_tokens(cache.desc, num_reqs, num_q_heads, max_chunk_len,
+                                          max_total_len)
+
+
+def pkv_prefill_workspace_bytes(cache: PagedCache, num_reqs: int, num_q_tokens: int,
+                                num_q_heads: int, max_chunk_len: int, max_total_len: int,
+                                split_tokens: int = 0) -> int:
+    return lib().pkv_prefill_workspace_bytes(cache.desc, num_reqs, num_q_tokens, num_q_heads,
+                                             max_chunk_len, max_total_len, split_tokens)
+
+
+def prefill_workspace(cache: PagedCache, num_reqs: int, num_q_tokens: int, num_q_heads: int,
+                      max_chunk_len: int, max_total_len: int,
+                      split_tokens: int = 0) -> Optional[torch.Tensor]:
+    """A device buffer of the size the prefill call needs (None if it needs none)."""
+    n = pkv_prefill_workspace_bytes(cache, num_reqs, num_q_tokens, num_q_heads, max_chunk_len,
+                                    max_total_len, split_tokens)
+    if n == 0:
+        return None
+    return torch.empty(n, dtype=torch.uint8, device=cache.k_pool.device)
+
+
 def pkv_paged_attn_chunked_prefill(cache: PagedCache, q: torch.Tensor, out: torch.Tensor,
                                    cu_q_lens: torch.Tensor, ctx_before: torch.Tensor,
                                    block_tables: torch.Tensor, max_chunk_len: int,
-                                   sm_scale: float, lse: Optional[torch.Tensor] = None,
+                                   max_total_len: int, sm_scale: float,
+                                   lse: Optional[torch.Tensor] = None, split_tokens: int = 0,
+                                   workspace: Optional[torch.Tensor] = None,
                                    stream=None) -> None:
-    """Causal chunked prefill over packed query rows [T][Hq][D]."""
+    """Causal chunked prefill over packed query rows [T][Hq][D] (key ranges
+    plus the log-sum-exp merge when the workspace holds several ranges)."""
     _need(q.dim() == 3 and q.is_contiguous(), "q must be contiguous [T][Hq][D]")
     _need(out.shape == q.shape and out.is_contiguous(), "out must be contiguous like q")
     for t, n in ((cu_q_lens, "cu_q_lens"), (ctx_before, "ctx_before"),
@@ -318,10 +348,11 @@ def pkv_paged_attn_chunked_prefill(cache: PagedCache, q: torch.Tensor, out: torc
     if lse is not None:
         _need(lse.dtype == torch.float32 and lse.shape == q.shape[:2] and lse.is_contiguous(),
               "lse must be float32 [T][Hq]")
+    wp, wb = _ws(workspace)
     _check(lib().pkv_paged_attn_chunked_prefill(
         cache.desc, _ptr(q), _code_of(q), _ptr(out), _code_of(out), _ptr(lse), _ptr(cu_q_lens),
         _ptr(ctx_before), _ptr(block_tables), block_tables.shape[1], R, q.shape[0], q.shape[1],
-        max_chunk_len, float(sm_scale), _stream(stream)))
+        max_chunk_len, max_total_len, float(sm_scale), split_tokens, wp, wb, _stream(stream)))
 
 
 def pkv_validate_block_tables(cache: PagedCache, block_tables: torch.Tensor, lens: torch.Tensor,

@@ -209,6 +209,78 @@ pkv_status prepare_decode(const pkv_cache_desc* cache, const void* q, int32_t q_
   return PKV_OK;
 }
 
+// Prefill key ranges.  Matrix-core path: about 3/5 of the longest context,
+// at least 1024 keys.  Rows of the longest requests then split into two
+// uneven ranges — halving the longest serial walk, which bounds a step whose
+// contexts differ widely — while shorter requests stay in one range and need
+// no merge.  Contexts of up to 1024 keys take one range.  F32 caches
+// (generic path) always take one range.
+int32_t default_prefill_split(const pkv_cache_desc* c, int32_t max_total) {
+  const int32_t one = std::max<int32_t>(64, (max_total + 63) / 64 * 64);
+  if (c->kv_dtype == PKV_F32) return one;
+  const int32_t part = (int32_t)(((int64_t)max_total * 3 / 5 + 63) / 64 * 64);
+  return std::min<int32_t>(one, std::max<int32_t>(1024, part));
+}
+
+size_t prefill_ws_bytes(const pkv_cache_desc* c, int32_t num_q_tokens, int32_t num_q_heads,
+                        int32_t ms) {
+  if (ms <= 1 || num_q_tokens <= 0) return 0;
+  const size_t n = (size_t)num_q_tokens * num_q_heads * ms;
+  const size_t acc = (n * c->head_dim * 4 + 255) / 256 * 256;
+  const size_t ml = (n * 2 * 4 + 255) / 256 * 256;
+  return acc + ml;
+}
+
+// Shape checks shared by the prefill call and its planning functions; fills
+// the size fields of `a` (pointers are left NULL).
+pkv_status prepare_prefill(const pkv_cache_desc* cache, int32_t q_dtype, int32_t out_dtype,
+                           int32_t num_reqs, int32_t num_q_tokens, int32_t num_q_heads,
+                           int32_t max_chunk_len, int32_t max_total_len, int32_t split_tokens,
+                           pkv::AttnArgs* a) {
+  pkv_status st;
+  if ((st = check_cache(cache)) != PKV_OK) return st;
+  if ((st = check_qo_dtypes(cache, q_dtype, out_dtype)) != PKV_OK) return st;
+  if ((st = check_heads(cache, num_q_heads)) != PKV_OK) return st;
+  if (num_reqs < 0 || num_q_tokens < 0 || max_chunk_len < 0 || max_total_len < 0 ||
+      split_tokens < 0)
+    return fail(PKV_ERR_INVALID_ARG, "negative size");
+  std::memset(a, 0, sizeof *a);
+  a->c = view(cache);
+  a->num_rows = num_reqs;
+  a->num_tokens = num_q_tokens;
+  a->max_chunk = max_chunk_len;
+  a->num_q_heads = num_q_heads;
+  a->prefill = 1;
+  a->page_shift = __builtin_ctz((unsigned)cache->page_size);
+  a->max_splits = 1;
+  a->split_tokens = 64;
+  if (num_q_tokens == 0 || num_reqs == 0) return PKV_OK;
+  if (max_chunk_len <= 0) return fail(PKV_ERR_INVALID_ARG, "max_chunk_len must be positive");
+  if (num_reqs > kMaxGridYZ) return fail(PKV_ERR_UNSUPPORTED, "num_reqs %d > %d", num_reqs, kMaxGridYZ);
+  if (max_total_len < max_chunk_len)
+    return fail(PKV_ERR_INVALID_ARG, "max_total_len %d < max_chunk_len %d", max_total_len,
+                max_chunk_len);
+  const int32_t split = split_tokens ? split_tokens : default_prefill_split(cache, max_total_len);
+  if (split % 64 != 0)
+    return fail(PKV_ERR_INVALID_ARG, "split_tokens %d is not a positive multiple of 64", split);
+  const int32_t ms = ceil_div(max_total_len, split);
+  if (ms > kMaxGridYZ)
+    return fail(PKV_ERR_UNSUPPORTED, "%d key ranges per row (max %d)", ms, kMaxGridYZ);
+  a->split_tokens = split;
+  a->max_splits = std::max(1, ms);
+  if (!pkv::prefill_mfma_supported(*a)) {
+    // generic path: one workgroup per (KV head, chunk row), one range
+    if (ms > 1)
+      return fail(PKV_ERR_UNSUPPORTED, "this cache takes one key range (split_tokens >= %d)",
+                  max_total_len);
+    if ((int64_t)num_reqs * max_chunk_len > kMaxGridYZ)
+      return fail(PKV_ERR_UNSUPPORTED, "num_reqs * max_chunk_len > %d", kMaxGridYZ);
+  } else if (pkv::prefill_mfma_grid(*a) > 0x7FFFFFFFLL) {
+    return fail(PKV_ERR_UNSUPPORTED, "prefill grid too large");
+  }
+  return PKV_OK;
+}
+
 }  // namespace
 
 namespace pkv_detail {
@@ -325,25 +397,26 @@ pkv_status pkv_paged_attn_chunked_prefill(const pkv_cache_desc* cache, const voi
                                           const int32_t* ctx_before, const int32_t* block_tables,
                                           int32_t bt_stride, int32_t num_reqs,
                                           int32_t num_q_tokens, int32_t num_q_heads,
-                                          int32_t max_chunk_len, float sm_scale, void* stream) {
-  pkv_status st;
-  if ((st = check_cache(cache)) != PKV_OK) return st;
-  if ((st = check_qo_dtypes(cache, q_dtype, out_dtype)) != PKV_OK) return st;
-  if ((st = check_heads(cache, num_q_heads)) != PKV_OK) return st;
-  if (num_reqs < 0 || num_q_tokens < 0 || max_chunk_len < 0)
-    return fail(PKV_ERR_INVALID_ARG, "negative size");
+                                          int32_t max_chunk_len, int32_t max_total_len,
+                                          float sm_scale, int32_t split_tokens, void* workspace,
+                                          size_t workspace_bytes_in, void* stream) {
+  pkv::AttnArgs a;
+  pkv_status st = prepare_prefill(cache, q_dtype, out_dtype, num_reqs, num_q_tokens, num_q_heads,
+                                  max_chunk_len, max_total_len, split_tokens, &a);
+  if (st != PKV_OK) return st;
   if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f))
     return fail(PKV_ERR_INVALID_ARG, "sm_scale must be finite and positive");
   if (num_q_tokens == 0 || num_reqs == 0) return PKV_OK;
   if (!q || !out || !cu_q_lens || !ctx_before || !block_tables)
     return fail(PKV_ERR_INVALID_ARG, "prefill pointers must not be NULL");
   if (bt_stride <= 0) return fail(PKV_ERR_INVALID_ARG, "bt_stride %d", bt_stride);
-  if (max_chunk_len <= 0) return fail(PKV_ERR_INVALID_ARG, "max_chunk_len must be positive");
-  if ((int64_t)num_reqs * max_chunk_len > kMaxGridYZ)
-    return fail(PKV_ERR_UNSUPPORTED, "num_reqs * max_chunk_len > %d", kMaxGridYZ);
-  pkv::AttnArgs a;
-  std::memset(&a, 0, sizeof a);
-  a.c = view(cache);
+  if ((int64_t)bt_stride * cache->page_size < max_total_len)
+    return fail(PKV_ERR_INVALID_ARG, "max_total_len %d exceeds bt_stride*page_size %lld",
+                max_total_len, (long long)bt_stride * cache->page_size);
+  const size_t need = prefill_ws_bytes(cache, num_q_tokens, num_q_heads, a.max_splits);
+  if (need > 0 && (!workspace || workspace_bytes_in < need))
+    return fail(PKV_ERR_INVALID_ARG, "workspace of %zu bytes needed, %zu given", need,
+                workspace_bytes_in);
   a.q = q;
   a.out = out;
   a.lse = lse;
@@ -351,17 +424,37 @@ pkv_status pkv_paged_attn_chunked_prefill(const pkv_cache_desc* cache, const voi
   a.bt_stride = bt_stride;
   a.cu_q = cu_q_lens;
   a.ctx_before = ctx_before;
-  a.num_rows = num_reqs;
-  a.max_chunk = max_chunk_len;
-  a.num_q_heads = num_q_heads;
-  const int64_t cap = (int64_t)bt_stride * cache->page_size;
-  a.split_tokens = (int32_t)std::min<int64_t>((cap + 15) / 16 * 16, (int64_t)1 << 30);
-  a.max_splits = 1;
   a.sm_scale = sm_scale;
-  a.prefill = 1;
-  a.page_shift = __builtin_ctz((unsigned)cache->page_size);
-  return hip_status(pkv::launch_prefill(a, static_cast<hipStream_t>(stream)),
-                    "paged_attn_chunked_prefill");
+  if (need > 0) {
+    char* w = static_cast<char*>(workspace);
+    const size_t n = (size_t)num_q_tokens * num_q_heads * a.max_splits;
+    a.ws_acc = reinterpret_cast<float*>(w);
+    a.ws_ml = reinterpret_cast<float*>(w + (n * cache->head_dim * 4 + 255) / 256 * 256);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = hip_status(pkv::launch_prefill(a, s), "paged_attn_chunked_prefill")) != PKV_OK)
+    return st;
+  return hip_status(pkv::launch_lse_merge(a, s), "paged_attn_chunked_prefill (merge)");
+}
+
+int32_t pkv_prefill_split_tokens(const pkv_cache_desc* cache, int32_t num_reqs,
+                                 int32_t num_q_heads, int32_t max_chunk_len,
+                                 int32_t max_total_len) {
+  if (check_cache(cache) != PKV_OK || check_heads(cache, num_q_heads) != PKV_OK) return 0;
+  if (num_reqs < 0 || max_chunk_len < 0 || max_total_len < max_chunk_len) return 0;
+  return default_prefill_split(cache, max_total_len);
+}
+
+size_t pkv_prefill_workspace_bytes(const pkv_cache_desc* cache, int32_t num_reqs,
+                                   int32_t num_q_tokens, int32_t num_q_heads,
+                                   int32_t max_chunk_len, int32_t max_total_len,
+                                   int32_t split_tokens) {
+  pkv::AttnArgs a;
+  const int32_t dt = cache && cache->kv_dtype == PKV_F32 ? PKV_F32 : PKV_BF16;
+  if (prepare_prefill(cache, dt, dt, num_reqs, num_q_tokens, num_q_heads, max_chunk_len,
+                      max_total_len, split_tokens, &a) != PKV_OK)
+    return 0;
+  return prefill_ws_bytes(cache, num_q_tokens, num_q_heads, a.max_splits);
 }
 
 pkv_status pkv_validate_block_tables(const pkv_cache_desc* cache, const int32_t* block_tables,

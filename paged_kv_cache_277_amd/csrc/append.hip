@@ -20,13 +20,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   constexpr int KVB = KvBytes<KVT>::value;
   constexpr int EPL = 16 / KVB;                  // cache elements per 16-byte piece
   const int t = blockIdx.x;
-  // Row r owning packed token t: the largest r with cu[r] <= t.
-  int lo = 0, hi = a.num_rows;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (a.cu[mid] <= t) lo = mid; else hi = mid;
-  }
-  const int r = lo;
+  const int r = owner_row(a.cu, a.num_rows, t);
   const int pos = a.start_pos[r] + (t - a.cu[r]);
   const int P = a.c.page_size;
   const int page = a.bt[(size_t)r * a.bt_stride + pos / P];

@@ -331,57 +331,75 @@ __global__ __launch_bounds__(256) void decode_partial_vec(AttnArgs a) {
 // each (the (m, l) pairs: max and weighted sum by wave reductions), then
 // cover head_dim and sum the weighted accumulators, four ranges per batch of
 // independent loads.
+// Log-sum-exp merge of per-range partials:
+//   M = max_s m_s,  w_s = exp2(m_s - M),  out = sum_s w_s acc_s / sum_s w_s l_s,
+//   lse = (M + log2 sum_s w_s l_s) ln 2      (m in log2 units)
+// Every thread owns one 16-byte chunk of one head's output: a workgroup
+// covers 256 / (D/4) heads of one row (8 at D = 128).  The grid is (row,
+// head group) for decode and (chunk row, head group, request) for prefill,
+// so a prefill workgroup reads its request's offsets directly.  A thread
+// reads its head's (m, l) pairs (the same
+// 8-byte words for the whole head, served from cache), forms the weights in
+// registers, then streams that head's partial accumulators — contiguous
+// [ranges][D] — four ranges at a time.  No LDS and no barrier: the chain per
+// thread is one round trip for (m, l) and one per four ranges.
+template <int D>
+__device__ __forceinline__ void store4(float* o, size_t i, f32x4 v) {
+  *reinterpret_cast<f32x4*>(o + i) = v;
+}
+template <int D>
+__device__ __forceinline__ void store4(uint16_t* o, size_t i, f32x4 v) {
+  *reinterpret_cast<u32x2*>(o + i) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+}
+
 template <typename OT, int D>
 __global__ __launch_bounds__(256) void lse_merge_kernel(AttnArgs a) {
-  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int Hq = a.num_q_heads;
-  if (wid >= a.num_rows * Hq) return;
-  const int z = wid / Hq, h = wid - z * Hq;
-  const int L = a.context_lens[z];
-  const int n = (L + a.split_tokens - 1) / a.split_tokens;
+  constexpr int C4 = D / 4;                      // 16-byte chunks per head
+  constexpr int HPW = 256 / C4;                  // heads per workgroup
+  const int h = blockIdx.y * HPW + threadIdx.x / C4;
+  const int d = 4 * (threadIdx.x % C4);
+  const int Hq = a.num_q_heads, ms = a.max_splits;
+  if (h >= Hq) return;
+  int z, L;
+  if (a.prefill) {
+    // Chunk row i of request r is packed row cu_q[r] + i, at absolute
+    // position ctx_before[r] + i: it attends that many keys plus itself.
+    const int r = blockIdx.z, i = blockIdx.x;
+    const int c0 = a.cu_q[r], c1 = a.cu_q[r + 1], pr = a.ctx_before[r];
+    if (i >= c1 - c0) return;
+    z = c0 + i;
+    L = pr + i + 1;
+  } else {
+    z = blockIdx.x;
+    L = a.context_lens[z];
+  }
+  const int n = min((L + a.split_tokens - 1) / a.split_tokens, ms);
   if (n <= 1) return;
-  const size_t base = ((size_t)z * Hq + h) * a.max_splits;
+  const size_t slot0 = ((size_t)z * Hq + h) * ms;
+  const f32x2* ml = reinterpret_cast<const f32x2*>(a.ws_ml) + slot0;
   float M = -INFINITY;
-  for (int s0 = 0; s0 < n; s0 += 64)
-    if (s0 + lane < n) M = fmaxf(M, a.ws_ml[(base + s0 + lane) * 2]);
-#pragma unroll
-  for (int msk = 32; msk >= 1; msk >>= 1) M = fmaxf(M, __shfl_xor(M, msk, 64));
+  for (int s = 0; s < n; ++s) M = fmaxf(M, ml[s][0]);
+  const float* acc = a.ws_acc + slot0 * D + d;
+  f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f};
   float den = 0.0f;
-  for (int s0 = 0; s0 < n; s0 += 64)
-    if (s0 + lane < n) {
-      const float m_s = a.ws_ml[(base + s0 + lane) * 2], l_s = a.ws_ml[(base + s0 + lane) * 2 + 1];
-      den = fmaf(l_s, __builtin_amdgcn_exp2f(m_s - M), den);
+  for (int s0 = 0; s0 < n; s0 += 4) {
+    f32x4 v[4];
+    f32x2 mlv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int ss = min(s0 + u, n - 1);         // clamped duplicates get weight 0
+      v[u] = *reinterpret_cast<const f32x4*>(acc + (size_t)ss * D);
+      mlv[u] = ml[ss];
     }
 #pragma unroll
-  for (int msk = 32; msk >= 1; msk >>= 1) den += __shfl_xor(den, msk, 64);
-  constexpr int PER = D / 64;
-  float o[PER];
-#pragma unroll
-  for (int k = 0; k < PER; ++k) o[k] = 0.0f;
-  for (int s0 = 0; s0 < n; s0 += 64) {
-    // weight of range s0 + lane, broadcast below by shuffles
-    const float wl = (s0 + lane < n) ? __builtin_amdgcn_exp2f(a.ws_ml[(base + s0 + lane) * 2] - M) : 0.0f;
-    const int cnt = min(64, n - s0);
-    for (int s = 0; s < cnt; s += 4) {
-      float acc[4][PER], wv[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int ss = min(s + u, cnt - 1);      // clamped duplicates get weight 0
-        wv[u] = (s + u < cnt) ? __shfl(wl, ss, 64) : 0.0f;
-#pragma unroll
-        for (int k = 0; k < PER; ++k) acc[u][k] = a.ws_acc[(base + s0 + ss) * D + lane + 64 * k];
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int k = 0; k < PER; ++k) o[k] = fmaf(acc[u][k], wv[u], o[k]);
+    for (int u = 0; u < 4; ++u) {
+      const float wgt = s0 + u < n ? __builtin_amdgcn_exp2f(mlv[u][0] - M) : 0.0f;
+      den = fmaf(mlv[u][1], wgt, den);
+      o += v[u] * wgt;
     }
   }
-  const float inv = 1.0f / den;
-#pragma unroll
-  for (int k = 0; k < PER; ++k) store_o<OT>(a.out, ((size_t)z * Hq + h) * D + lane + 64 * k, o[k] * inv);
-  if (lane == 0 && a.lse) a.lse[(size_t)z * Hq + h] = (M + __log2f(den)) * kLn2;
+  store4<D>(static_cast<OT*>(a.out), ((size_t)z * Hq + h) * D + d, o * (1.0f / den));
+  if (d == 0 && a.lse) a.lse[(size_t)z * Hq + h] = (M + __log2f(den)) * kLn2;
 }
 
 template <int KVT, int D>
@@ -419,10 +437,13 @@ hipError_t launch_decode_partial(const AttnArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_lse_merge(const AttnArgs& a, hipStream_t s) {
-  if (a.num_rows == 0 || a.max_splits <= 1) return hipSuccess;
-  const int waves = a.num_rows * a.num_q_heads;
-  const dim3 grid((waves + 3) / 4), block(256);
+  const int rows = a.prefill ? a.num_tokens : a.num_rows;
+  if (a.num_rows == 0 || rows == 0 || a.max_splits <= 1) return hipSuccess;
   const bool f32 = a.c.kv_dtype == KV_F32;
+  const int hpw = 256 / (a.c.head_dim / 4);
+  const int groups = (a.num_q_heads + hpw - 1) / hpw;
+  const dim3 grid = a.prefill ? dim3(a.max_chunk, groups, a.num_rows) : dim3(rows, groups);
+  const dim3 block(256);
   if (a.c.head_dim == 64) {
     if (f32) hipLaunchKernelGGL((lse_merge_kernel<float, 64>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((lse_merge_kernel<uint16_t, 64>), grid, block, 0, s, a);

@@ -49,7 +49,6 @@ constexpr int kMaxRangePages = 512;            // block-table entries staged per
 
 typedef __bf16 bf16x8_t __attribute__((__vector_size__(16)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),

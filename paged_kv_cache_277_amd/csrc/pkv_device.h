@@ -26,6 +26,7 @@ template <> struct KvBytes<KV_BF16> { static constexpr int value = 2; };
 template <> struct KvBytes<KV_FP8> { static constexpr int value = 1; };
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -144,5 +145,16 @@ __device__ __forceinline__ void settle(const u32x4& x) { asm volatile("" ::"v"(x
 
 // Wave-uniform copy of a value (lets the compiler keep it in an SGPR).
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Request owning packed token t: the largest r < n with cu[r] <= t
+// (cu[0] = 0, non-decreasing, n >= 1).
+__device__ __forceinline__ int owner_row(const int32_t* cu, int n, int t) {
+  int lo = 0, hi = n;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cu[mid] <= t) lo = mid; else hi = mid;
+  }
+  return lo;
+}
 
 }  // namespace pkv

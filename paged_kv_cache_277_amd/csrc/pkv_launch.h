@@ -41,12 +41,13 @@ struct AttnArgs {
   const int32_t* cu_q;           // prefill
   const int32_t* ctx_before;     // prefill
   int32_t num_rows;              // decode: sequences; prefill: requests
+  int32_t num_tokens;            // prefill: packed query tokens (rows of out / workspace)
   int32_t max_chunk;             // prefill: longest chunk
   int32_t num_q_heads;
   int32_t split_tokens;
   int32_t max_splits;
   float sm_scale;
-  float* ws_acc;                 // [rows][Hq][max_splits][D]
+  float* ws_acc;                 // [rows][Hq][max_splits][D]   (prefill rows: tokens)
   float* ws_ml;                  // [rows][Hq][max_splits][2]
   int32_t prefill;
   int32_t page_shift;            // log2(page_size)
@@ -61,6 +62,7 @@ bool decode_mfma_supported(const AttnArgs& a);
 hipError_t launch_decode_partial_mfma(const AttnArgs& a, hipStream_t s);
 // Chunked prefill on the matrix cores (bf16 queries, bf16 or fp8 KV).
 bool prefill_mfma_supported(const AttnArgs& a);
+long long prefill_mfma_grid(const AttnArgs& a);    // workgroups of one launch
 hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t s);
 hipError_t launch_fp8_to_f32(const uint8_t* codes, float* out, int64_t n, hipStream_t s);
 

@@ -10,11 +10,15 @@
 // Work decomposition (MI355X): the G query heads that share KV head j, times
 // the chunk's tokens, form "rows" (row = token*G + head).  A workgroup owns 128
 // consecutive rows of one (request, KV head) — 32 per wave, two MFMA N-tiles
-// that share every K and V^T operand read from LDS — and walks the keys 0 .. (its last row's position) in 32-token tiles.  Each
-// K/V tile is fetched from the pages once per workgroup into LDS and shared by
-// the four waves; loads run three tiles ahead of the compute (register
-// staging, double-buffered LDS), with the request's block-table entries
-// staged in LDS so no load waits on another:
+// that share every K and V^T operand read from LDS — and one range of
+// split_tokens keys out of 0 .. (its last row's position), walked in 32-token
+// tiles.  Long contexts thus spread over several workgroups instead of one
+// long serial walk; rows whose keys span several ranges leave (m, l, acc)
+// partials that the log-sum-exp merge combines, the same way split decode
+// does.  Each K/V tile is fetched from the pages once per workgroup into LDS
+// and shared by the four waves; loads run three tiles ahead of the compute
+// (register staging, double-buffered LDS), with the range's block-table
+// entries staged in LDS so no load waits on another:
 //
 //   S^T[t][row] = sum_d K[t][d] Q[row][d]    A = K from LDS (16-byte reads),
 //                                            B = Q^T in registers
@@ -42,7 +46,6 @@ constexpr int kMaxPages = 512;              // block-table entries staged per wo
 
 typedef __bf16 bf16x8_t __attribute__((__vector_size__(16)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -71,8 +74,8 @@ struct PfRegs {
 
 template <int KVT, int D>
 __device__ __forceinline__ void pf_load(PfRegs<KVT, D>& r, const uint8_t* kp, const uint8_t* vp,
-                                        const int32_t* pages, int t0, int kmax, int Hkv, int j,
-                                        int pshift) {
+                                        const int32_t* pages, int pg0, int t0, int kmax, int Hkv,
+                                        int j, int pshift) {
   // Every call issues the same loads: pieces past kmax (or past the tile)
   // read the first 16 bytes of the pools instead, and pf_store zeroes them.
   // A fixed load count keeps the waits for older tiles exact.
@@ -85,7 +88,7 @@ __device__ __forceinline__ void pf_load(PfRegs<KVT, D>& r, const uint8_t* kp, co
     const int tok = piece / PR, pc = piece % PR;
     const int t = t0 + tok;
     const bool ok = piece < S::PIECES && t < kmax;
-    const int page = ok ? pages[t >> pshift] : 0;
+    const int page = ok ? pages[(t >> pshift) - pg0] : 0;
     const size_t off = ok ? ((((size_t)page * Hkv + j) << pshift | (size_t)(t & pmask)) * S::ROWB) +
                                 (size_t)pc * 16
                           : 0;
@@ -94,7 +97,7 @@ __device__ __forceinline__ void pf_load(PfRegs<KVT, D>& r, const uint8_t* kp, co
   }
 }
 
-// Registers -> LDS (bf16 rows, padded); rows at or past kmax become zeros
+// Registers -> LDS (bf16 rows, padded); rows at or past kmax (the range end) become zeros
 // (masked keys must carry finite values: their probability is exactly 0).
 template <int KVT, int D>
 __device__ __forceinline__ void pf_store(PfRegs<KVT, D> r, uint8_t* kl, uint8_t* vl, int t0,
@@ -137,8 +140,15 @@ __device__ __forceinline__ void pf_store(PfRegs<KVT, D> r, uint8_t* kl, uint8_t*
   }
 }
 
+// A row's running max moves only when one of its scores exceeds it by more
+// than this (log2 units): until then probabilities are taken against the
+// older, smaller max and stay below 2^kSlack — well inside fp32 and bf16
+// range — and both the cross-lane max and the O / l rescale are skipped.
+// The final (m, l, acc) describes the same softmax whichever shift was used.
+constexpr float kSlack = 8.0f;
+
 template <int KVT, int D>
-__global__ __launch_bounds__(256, 2) void prefill_mfma(AttnArgs a, int nqb) {
+__global__ __launch_bounds__(256, 2) void prefill_mfma(AttnArgs a, int nqb, int npg) {
   using S = PfShape<KVT, D>;
   constexpr int KK = D / 32, DT = D / 16;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * S::STAGE + kMaxPages * 4];
@@ -147,12 +157,16 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma(AttnArgs a, int nqb) {
   // XCD-aware order: the hardware places workgroup b on XCD b % 8.  Pair
   // p = (request, KV head) goes to XCD p % 8 — all query blocks of a pair
   // share that XCD's L2, and consecutive pairs (the heads of one request)
-  // spread over all XCDs so no XCD gets one request's whole load.  Grid size
-  // is 8 * ceil(pairs / 8) * nqb; ids past the last pair exit.
+  // spread over all XCDs so no XCD gets one request's whole load.  Within an
+  // XCD the order is key range (outermost), pair group, then query block
+  // from the last (heaviest) down.  Grid size is 8 * npg * nqb * ranges with
+  // npg = ceil(pairs / 8); items past the last pair or the block's keys exit.
   const int b = blockIdx.x;
   const int xcd = b % 8, k = b / 8;
-  const int pair = (k / nqb) * 8 + xcd;
-  const int qb_rev = k % nqb;
+  const int per_range = npg * nqb;
+  const int rng = k / per_range, kr = k - rng * per_range;
+  const int pair = (kr / nqb) * 8 + xcd;
+  const int qb_rev = kr % nqb;
   if (pair >= a.num_rows * Hkv) return;
   const int j = pair % Hkv, r = pair / Hkv;
   const int c0 = a.cu_q[r], C = a.cu_q[r + 1] - c0;
@@ -161,7 +175,10 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma(AttnArgs a, int nqb) {
   if (row0 >= C * G) return;
   const int Pr = a.ctx_before[r];
   const int last_row = min(C * G, row0 + kRows) - 1;
-  const int kmax = Pr + last_row / G + 1;        // keys needed by the block's last row
+  const int kneed = Pr + last_row / G + 1;       // keys needed by the block's last row
+  const int t_begin = rng * a.split_tokens;      // this workgroup's key range
+  if (t_begin >= kneed) return;
+  const int kmax = min(kneed, t_begin + a.split_tokens);
 
   const int lane = threadIdx.x & 63;
   const int w = uniform(threadIdx.x >> 6);
@@ -212,13 +229,15 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma(AttnArgs a, int nqb) {
   const int32_t* btrow = a.bt + (size_t)r * a.bt_stride;
   const uint8_t* kp = static_cast<const uint8_t*>(a.c.k_pool);
   const uint8_t* vp = static_cast<const uint8_t*>(a.c.v_pool);
-  const int ntiles = (kmax + kTile - 1) / kTile;
+  const int ntiles = (kmax - t_begin + kTile - 1) / kTile;
   const int pshift = a.page_shift;
 
-  // The request's block-table entries for keys 0..kmax-1, staged in LDS once.
+  // The block-table entries for keys t_begin .. kmax-1, staged in LDS once;
+  // pf_load indexes them by absolute page number minus pg0.
   int32_t* pages = reinterpret_cast<int32_t*>(smem + 2 * S::STAGE);
-  const int npages = (kmax + (1 << pshift) - 1) >> pshift;
-  for (int i = threadIdx.x; i < npages; i += blockDim.x) pages[i] = btrow[i];
+  const int pg0 = t_begin >> pshift;
+  const int npages = ((kmax - 1) >> pshift) - pg0 + 1;
+  for (int i = threadIdx.x; i < npages; i += blockDim.x) pages[i] = btrow[pg0 + i];
   __syncthreads();
 
   // Pipeline: tile t is staged in register set t % 3 and LDS buffer t % 2.
@@ -226,17 +245,17 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma(AttnArgs a, int nqb) {
   // and tile i+1 (loaded two steps earlier) is written to the other LDS
   // buffer, so each load has two compute steps to land.
   PfRegs<KVT, D> r0, r1, r2;
-  pf_load<KVT, D>(r0, kp, vp, pages, 0, kmax, Hkv, j, pshift);
-  pf_load<KVT, D>(r1, kp, vp, pages, kTile, kmax, Hkv, j, pshift);
-  pf_load<KVT, D>(r2, kp, vp, pages, 2 * kTile, kmax, Hkv, j, pshift);
-  pf_store<KVT, D>(r0, smem, smem + kTile * S::K_LDS, 0, kmax);
+  pf_load<KVT, D>(r0, kp, vp, pages, pg0, t_begin, kmax, Hkv, j, pshift);
+  pf_load<KVT, D>(r1, kp, vp, pages, pg0, t_begin + kTile, kmax, Hkv, j, pshift);
+  pf_load<KVT, D>(r2, kp, vp, pages, pg0, t_begin + 2 * kTile, kmax, Hkv, j, pshift);
+  pf_store<KVT, D>(r0, smem, smem + kTile * S::K_LDS, t_begin, kmax);
   __syncthreads();
 
   auto step = [&](int it, PfRegs<KVT, D>& rfree, const PfRegs<KVT, D>& rnext) {
-    const int t0 = it * kTile;
+    const int t0 = t_begin + it * kTile;
     uint8_t* kl = smem + (it & 1) * S::STAGE;
     uint8_t* vl = kl + kTile * S::K_LDS;
-    pf_load<KVT, D>(rfree, kp, vp, pages, t0 + 3 * kTile, kmax, Hkv, j, pshift);
+    pf_load<KVT, D>(rfree, kp, vp, pages, pg0, t0 + 3 * kTile, kmax, Hkv, j, pshift);
 
     if (t0 < wave_kmax) {                        // skip tiles wholly above this wave's diagonal
       // ---- S^T for the two 16-key blocks; each K operand feeds every N-tile ----
@@ -270,25 +289,31 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma(AttnArgs a, int nqb) {
             for (int rr = 0; rr < 4; ++rr)
               if (t0 + 16 * blk + 4 * g4 + rr > my_lim[nt]) sv[4 * blk + rr] = -INFINITY;
         }
+        // Each lane checks its own 8 scores against the row's running max;
+        // only when some score exceeds it by more than kSlack (always on a
+        // row's first visible key, rarely afterwards) does the wave reduce
+        // the row max over the row's 4 lanes and rescale.  A row whose keys
+        // all lie past this range's start sees only masked keys: its m stays
+        // -inf and every p below is exp2(-inf) = 0.
         float mx = sv[0];
 #pragma unroll
         for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        // Key 0 is visible to every row (padding rows included), so mx is
-        // finite on the first tile and m stays finite afterwards.
-        const float mn = fmaxf(m[nt], mx * smul);
-        if (__any(mn > m[nt])) {                 // rescale only when some row's max grew
-          const float alpha = __builtin_amdgcn_exp2f(m[nt] - mn);
+        if (__any(mx * smul > m[nt] + kSlack)) {
+          mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+          mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+          const float mn = fmaxf(m[nt], mx * smul);
+          // (a row still at -inf has l = 0 and O = 0: any finite factor will do)
+          const float alpha = m[nt] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m[nt] - mn);
           l[nt] *= alpha;
 #pragma unroll
           for (int i = 0; i < DT; ++i) o[nt][i] *= alpha;
           m[nt] = mn;
         }
+        const float msub = m[nt] == -INFINITY ? 0.0f : m[nt];
         float p[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          p[i] = __builtin_amdgcn_exp2f(fmaf(sv[i], smul, -m[nt]));
+          p[i] = __builtin_amdgcn_exp2f(fmaf(sv[i], smul, -msub));
           l[nt] += p[i];
         }
         pb[nt][0] = pack_bf16x2(p[0], p[1]);
@@ -326,13 +351,18 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma(AttnArgs a, int nqb) {
     if (it + 2 < ntiles) step(it + 2, r2, r0);
   }
 
-  // ---- finish rows: l is split over the 4 lanes of a row ----
+  // ---- finish rows: l is split over the 4 lanes of a row.  A row whose
+  // keys fit one range (L <= split_tokens) is final here; otherwise this
+  // range's (m, l, acc) goes to the workspace for the merge, if the row has
+  // keys in it. ----
 #pragma unroll
   for (int nt = 0; nt < kNt; ++nt) {
     float lt = l[nt];
     lt += __shfl_xor(lt, 16, 64);
     lt += __shfl_xor(lt, 32, 64);
-    if (row_ok[nt]) {
+    const int L = my_lim[nt] + 1;                // keys this row attends
+    const bool single = L <= a.split_tokens;     // all of them in range 0
+    if (row_ok[nt] && single && rng == 0) {
       const float inv = vscale / lt;
       uint16_t* out = static_cast<uint16_t*>(a.out) + row_off[nt];
 #pragma unroll
@@ -342,31 +372,47 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma(AttnArgs a, int nqb) {
         *reinterpret_cast<u32x2*>(out + 16 * dt + 4 * g4) = u32x2{lo, hi};
       }
       if (g4 == 0 && a.lse) a.lse[row_off[nt] / D] = (m[nt] + __log2f(lt)) * kLn2;
+    } else if (row_ok[nt] && !single && t_begin < L) {
+      const size_t slot = (row_off[nt] / D) * a.max_splits + rng;
+      float* acc = a.ws_acc + slot * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        *reinterpret_cast<f32x4*>(acc + 16 * dt + 4 * g4) = o[nt][dt] * vscale;
+      if (g4 == 0) { a.ws_ml[slot * 2] = m[nt]; a.ws_ml[slot * 2 + 1] = lt; }
     }
   }
 }
 
 }  // namespace
 
+// The block-table slice of one key range must fit the LDS staging area: a
+// range of split_tokens keys touches at most split/page + 1 pages.
 bool prefill_mfma_supported(const AttnArgs& a) {
   return a.prefill && a.c.kv_dtype != KV_F32 && (a.c.head_dim == 64 || a.c.head_dim == 128) &&
-         a.bt_stride <= kMaxPages;
+         a.split_tokens % kTile == 0 && (a.split_tokens >> a.page_shift) + 1 <= kMaxPages;
+}
+
+long long prefill_mfma_grid(const AttnArgs& a) {
+  const int G = a.num_q_heads / a.c.num_kv_heads;
+  const long long nqb = ((long long)a.max_chunk * G + kRows - 1) / kRows;
+  const long long pairs = (long long)a.c.num_kv_heads * a.num_rows;
+  return (pairs + 7) / 8 * 8 * nqb * a.max_splits;
 }
 
 hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t s) {
   const int G = a.num_q_heads / a.c.num_kv_heads;
   const int nqb = (a.max_chunk * G + kRows - 1) / kRows;
-  const long long pairs = (long long)a.c.num_kv_heads * a.num_rows;
-  const long long nwg = (pairs + 7) / 8 * 8 * nqb;
+  const int npg = (a.c.num_kv_heads * a.num_rows + 7) / 8;
+  const long long nwg = prefill_mfma_grid(a);
   if (nwg == 0) return hipSuccess;
   if (nwg > 0x7FFFFFFFLL) return hipErrorInvalidValue;
   const dim3 grid((unsigned)nwg), block(256);
   if (a.c.kv_dtype == KV_BF16) {
-    if (a.c.head_dim == 128) hipLaunchKernelGGL((prefill_mfma<KV_BF16, 128>), grid, block, 0, s, a, nqb);
-    else hipLaunchKernelGGL((prefill_mfma<KV_BF16, 64>), grid, block, 0, s, a, nqb);
+    if (a.c.head_dim == 128) hipLaunchKernelGGL((prefill_mfma<KV_BF16, 128>), grid, block, 0, s, a, nqb, npg);
+    else hipLaunchKernelGGL((prefill_mfma<KV_BF16, 64>), grid, block, 0, s, a, nqb, npg);
   } else {
-    if (a.c.head_dim == 128) hipLaunchKernelGGL((prefill_mfma<KV_FP8, 128>), grid, block, 0, s, a, nqb);
-    else hipLaunchKernelGGL((prefill_mfma<KV_FP8, 64>), grid, block, 0, s, a, nqb);
+    if (a.c.head_dim == 128) hipLaunchKernelGGL((prefill_mfma<KV_FP8, 128>), grid, block, 0, s, a, nqb, npg);
+    else hipLaunchKernelGGL((prefill_mfma<KV_FP8, 64>), grid, block, 0, s, a, nqb, npg);
   }
   return hipGetLastError();
 }

@@ -107,8 +107,9 @@ class DeviceWorkload:
             return
         p = self.pf
         B.pkv_paged_attn_chunked_prefill(self.cache, p["q"], p["out"], p["cu"], p["ctx"], p["bt"],
-                                         p["max_chunk"], float(self.wl.sm_scale), lse=p["lse"],
-                                         stream=stream)
+                                         p["max_chunk"], p["max_total"], float(self.wl.sm_scale),
+                                         lse=p["lse"], split_tokens=p["split"],
+                                         workspace=p["ws"], stream=stream)
 
     def step(self, stream=None) -> None:
         """One pass of the hot path: append -> decode (partial + merge) -> prefill."""
@@ -116,8 +117,30 @@ class DeviceWorkload:
         self.decode(stream)
         self.prefill(stream)
 
+    def capture_step(self) -> "torch.cuda.CUDAGraph":
+        """Record one step (every launch of `step`) as a HIP graph.
 
-def upload(wl: Workload, device="cuda", split_tokens: int = 0) -> DeviceWorkload:
+        The library launches only kernels on the caller's stream and allocates
+        nothing, so stream capture records the whole step; replaying the graph
+        re-runs the same kernels on the same buffers with one launch.  (A CUDA
+        graph captured per batch shape is the pages' own remedy for launch
+        overhead in small decode steps: "TensorRT-LLM框架解析与高性能推理优化实践"
+        §8.1.)"""
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):          # warm the capture stream once
+            self.step()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.step()
+        torch.cuda.synchronize()
+        return g
+
+
+def upload(wl: Workload, device="cuda", split_tokens: int = 0,
+           prefill_split: int = 0) -> DeviceWorkload:
     s = wl.spec
     kp = poisoned_pool(wl.num_pages, s.num_kv_heads, s.page_size, s.head_dim, s.kv_dtype, device)
     vp = poisoned_pool(wl.num_pages, s.num_kv_heads, s.page_size, s.head_dim, s.kv_dtype, device)
@@ -147,11 +170,19 @@ def upload(wl: Workload, device="cuda", split_tokens: int = 0) -> DeviceWorkload
                         split_tokens=split, workspace=ws)
     if wl.num_prefill:
         pq = _dev(wl.pf_q, s.q_dtype, device)
+        chunk = np.diff(wl.pf_cu)
+        max_chunk = int(chunk.max())
+        max_total = int((wl.pf_ctx_before + chunk).max())
+        R, T = wl.num_prefill, pq.shape[0]
+        psplit = prefill_split or B.pkv_prefill_split_tokens(cache, R, s.num_q_heads, max_chunk,
+                                                             max_total)
         dw.pf = dict(q=pq, out=torch.empty_like(pq),
                      lse=torch.empty(pq.shape[:2], dtype=torch.float32, device=device),
                      cu=_dev(wl.pf_cu, "i32", device), ctx=_dev(wl.pf_ctx_before, "i32", device),
                      bt=_dev(wl.pf_block_tables, "i32", device),
-                     max_chunk=int(np.diff(wl.pf_cu).max()))
+                     max_chunk=max_chunk, max_total=max_total, split=psplit,
+                     ws=B.prefill_workspace(cache, R, T, s.num_q_heads, max_chunk, max_total,
+                                            psplit))
     return dw
 
 

@@ -181,13 +181,50 @@ def test_append_and_prefill_reject_on_host():
     # nothing to do is OK and launches nothing
     assert lib.pkv_kv_cache_append(C.byref(d), None, None, B.PKV_BF16, None, None, None, 0, 0, 0,
                                    None) == B.PKV_OK
-    assert lib.pkv_paged_attn_chunked_prefill(C.byref(d), FAKE, B.PKV_BF16, FAKE, B.PKV_BF16, None,
-                                              FAKE, FAKE, FAKE, 4, 2, 8, 5, 4, 0.1,
-                                              None) == B.PKV_ERR_INVALID_ARG   # Hq 5
-    assert lib.pkv_paged_attn_chunked_prefill(C.byref(d), FAKE, B.PKV_BF16, FAKE, B.PKV_BF16, None,
-                                              FAKE, FAKE, FAKE, 4, 2000, 8, 4, 100, 0.1,
-                                              None) == B.PKV_ERR_UNSUPPORTED   # grid too large
+    assert _prefill(d, Hq=5) == B.PKV_ERR_INVALID_ARG                 # 5 % 2 != 0
+    assert _prefill(d, max_total=3, max_chunk=4) == B.PKV_ERR_INVALID_ARG   # total < chunk
+    assert _prefill(d, max_total=65, stride=4) == B.PKV_ERR_INVALID_ARG     # > 4 pages * 16
+    assert _prefill(d, split=96 + 16) == B.PKV_ERR_INVALID_ARG        # not a multiple of 64
+    assert _prefill(d, scale=0.0) == B.PKV_ERR_INVALID_ARG
+    # two ranges of 32 keys need a workspace
+    assert _prefill(d, split=64, max_total=64 * 2, stride=8) == B.PKV_ERR_INVALID_ARG
+    assert b"workspace" in lib.pkv_last_error()
+    # the generic (f32) path takes one range only
+    f32 = _desc(kv_dtype=B.PKV_F32)
+    assert _prefill(f32, dt=B.PKV_F32, split=64, max_total=128, stride=8, ws=FAKE,
+                    wsb=1 << 30) == B.PKV_ERR_UNSUPPORTED
+    assert _prefill(f32, dt=B.PKV_F32, R=2000, max_chunk=100, max_total=100, stride=8,
+                    T=8) == B.PKV_ERR_UNSUPPORTED                      # grid too large
+    # nothing to do is OK
+    assert _prefill(d, T=0) == B.PKV_OK
     assert lib.pkv_fp8_e4m3fn_to_f32(FAKE + 1, FAKE, 8, None) == B.PKV_ERR_INVALID_ARG
+
+
+def _prefill(desc, dt=B.PKV_BF16, R=2, T=8, Hq=4, max_chunk=4, max_total=16, stride=4, split=0,
+             ws=None, wsb=0, scale=0.1):
+    return B.lib().pkv_paged_attn_chunked_prefill(C.byref(desc), FAKE, dt, FAKE, dt, None, FAKE,
+                                                  FAKE, FAKE, stride, R, T, Hq, max_chunk,
+                                                  max_total, scale, split, ws, wsb, None)
+
+
+def test_prefill_split_and_workspace_planning():
+    lib = B.lib()
+    d = _desc(head_dim=128, page_size=32, num_kv_heads=8, num_pages=4000)
+    split = lib.pkv_prefill_split_tokens(C.byref(d), 4, 32, 512, 2560)
+    assert split > 0 and split % 64 == 0 and split < 2560
+    ms = -(-2560 // split)
+    ws = lib.pkv_prefill_workspace_bytes(C.byref(d), 4, 2048, 32, 512, 2560, 0)
+    assert ws >= 2048 * 32 * ms * (128 + 2) * 4
+    # contexts that fit one range need no workspace
+    assert lib.pkv_prefill_workspace_bytes(C.byref(d), 4, 2048, 32, 512, 512, 0) == 0
+    assert lib.pkv_prefill_workspace_bytes(C.byref(d), 4, 2048, 32, 512, 2560, 2560 + 64) == 0
+    # f32 caches: always one range
+    f32 = _desc(kv_dtype=B.PKV_F32, num_pages=4000)
+    assert lib.pkv_prefill_split_tokens(C.byref(f32), 4, 4, 512, 2560) >= 2560
+    assert lib.pkv_prefill_workspace_bytes(C.byref(f32), 4, 2048, 4, 512, 2560, 0) == 0
+    # invalid -> 0
+    assert lib.pkv_prefill_split_tokens(C.byref(d), 4, 33, 512, 2560) == 0
+    assert lib.pkv_prefill_split_tokens(C.byref(d), 4, 32, 512, 100) == 0
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -244,12 +244,17 @@ PREFILL_CASES = [
 ]
 
 
+@pytest.mark.parametrize("psplit", [0, 64])
 @pytest.mark.parametrize("case", PREFILL_CASES)
-def test_prefill_parity_small(case):
+def test_prefill_parity_small(case, psplit):
+    """psplit 64 cuts every context longer than 64 keys into ranges (partials
+    + merge); 0 takes the library's default (one range at these sizes)."""
     lens, Hq, Hkv, D, P, kv, ctx, chunk = case
     spec = spec_of(lens, Hq, Hkv, D, P, kv, prefill_ctx=ctx, prefill_chunk=chunk)
     wl = wk.make_workload(spec, seed=41)
-    dw = dev.upload(wl)
+    if kv == "f32":
+        psplit = 0                                  # the generic path takes one range
+    dw = dev.upload(wl, prefill_split=psplit)
     dw.setup()
     dw.step()
     torch.cuda.synchronize()
@@ -259,6 +264,35 @@ def test_prefill_parity_small(case):
     check_lse(dw.pf["lse"], ref_lse, spec)
     dref, dlse = sup.oracle_decode(wl, kp, vp)
     check_close(dw.out, dref, spec, "decode")
+
+
+def test_prefill_ranges_loose_bound_and_invariance():
+    """A loose max_total_len bound (more ranges than any row needs) gives the
+    same rows as the exact one; range sizes change only rounding."""
+    spec = spec_of((9,), 16, 4, 128, 32, "bf16", prefill_ctx=(0, 300, 700), prefill_chunk=150)
+    wl = wk.make_workload(spec, seed=43)
+    dw = dev.upload(wl)
+    dw.setup()
+    dw.append_step()
+    p = dw.pf
+    kp, vp = sup.oracle_pools(wl)
+    ref, ref_lse = sup.oracle_prefill(wl, kp, vp)
+    outs = []
+    for split, total in ((64, p["max_total"]), (64, p["max_total"] + 400), (256, p["max_total"]),
+                         (1024, p["max_total"])):
+        total = min(total, wl.pf_block_tables.shape[1] * spec.page_size)
+        ws = B.prefill_workspace(dw.cache, wl.num_prefill, p["q"].shape[0], spec.num_q_heads,
+                                 p["max_chunk"], total, split)
+        out = torch.full_like(p["out"], float("nan"))
+        lse = torch.full_like(p["lse"], float("nan"))
+        B.pkv_paged_attn_chunked_prefill(dw.cache, p["q"], out, p["cu"], p["ctx"], p["bt"],
+                                         p["max_chunk"], total, float(wl.sm_scale), lse=lse,
+                                         split_tokens=split, workspace=ws)
+        torch.cuda.synchronize()
+        check_close(out, ref, spec, f"prefill split {split} bound {total}")
+        check_lse(lse, ref_lse, spec)
+        outs.append(out)
+    assert torch.equal(outs[0], outs[1]), "a looser bound changed the result"
 
 
 # ---------------------------------------------- the workloads at full size --
@@ -307,3 +341,38 @@ def test_mixed_step_full_size():
     check_close(dw.pf["out"][t], pref, spec, "prefill")
     check_lse(dw.pf["lse"][t], plse, spec)
     assert torch.isfinite(dw.pf["out"].float()).all()
+
+
+# ---------------------------------------------------------- graph replay ----
+@pytest.mark.parametrize("cfg", [1, 5])
+def test_step_graph_replays_match_eager(cfg):
+    """The captured step, replayed several times with eager work in between,
+    reproduces the eager step bit for bit (outputs cleared before each replay)."""
+    wl = wk.make_workload(wk.CONFIGS[cfg]) if cfg == 1 else wk.make_workload(
+        spec_of((40, 300, 1000), 32, 8, 128, 32, "bf16", prefill_ctx=(0, 100), prefill_chunk=70),
+        seed=5)
+    dw = dev.upload(wl)
+    dw.setup()
+    dw.step()
+    torch.cuda.synchronize()
+    ref_out, ref_lse = dw.out.clone(), dw.lse.clone()
+    ref_pf = dw.pf["out"].clone() if dw.pf else None
+    g = dw.capture_step()
+    for rep in range(3):
+        dw.out.zero_()
+        dw.lse.zero_()
+        if dw.pf:
+            dw.pf["out"].zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dw.out, ref_out), f"replay {rep}: decode output differs"
+        assert torch.equal(dw.lse, ref_lse)
+        if dw.pf:
+            assert torch.equal(dw.pf["out"], ref_pf), f"replay {rep}: prefill output differs"
+        dw.step()                                   # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(dw.out, ref_out)
+    kp, vp = sup.oracle_pools(wl)
+    ref, _ = sup.oracle_decode(wl, kp, vp)
+    check_close(dw.out, ref, wl.spec)
