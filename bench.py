@@ -7,10 +7,13 @@ Inputs are seeded synthetic data, resident in HBM before timing starts.
 
 Default workload: Llama-2-13B-shaped MHA decode in bf16 (64 sequences,
 40/40 heads, head_dim 128, page 64, context lengths uniform in [128, 4096]).
-Prints one JSON line: achieved HBM GB/s of the whole step (algorithmic bytes
-/ step time), seq-steps/s, the decode-partial kernel's roofline (its own
-event-timed duration inside the timed loop) and the CPU oracle timed on a
-bounded sample of the same workload.
+By default a step is one pkv_mixed_step call (append, then decode and, for
+a mixed workload, prefill on a second stream); --launch selects separate
+calls or HIP-graph replays instead.  Prints one JSON line: achieved HBM GB/s
+of the whole step (algorithmic bytes / step time), seq-steps/s, the
+decode-partial kernel's roofline (its own event-timed duration: inside the
+timed loop with --launch calls, else in an eager loop after it) and the CPU
+oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -131,8 +134,11 @@ def main() -> int:
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--graph", action="store_true",
-                    help="time replays of the step captured as one HIP graph")
+    ap.add_argument("--launch", choices=("mixed_step", "calls", "graph", "graph_mixed_step"),
+                    default="mixed_step",
+                    help="mixed_step: one pkv_mixed_step call per step, prefill on a second "
+                         "stream; calls: append, decode and prefill calls one after another; "
+                         "graph / graph_mixed_step: replays of those captured as a HIP graph")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain device copy of known size instead (counter scaling)")
     args = ap.parse_args()
@@ -161,20 +167,27 @@ def main() -> int:
     torch.cuda.synchronize()
     print(f"[bench] uploaded, split_tokens={dw.split_tokens}", file=sys.stderr, flush=True)
 
+    side = torch.cuda.Stream() if args.launch.endswith("mixed_step") else None
     for _ in range(args.warmup):
-        dw.step()
+        if side is not None:
+            dw.mixed_step(side_stream=side)
+        else:
+            dw.step()
     torch.cuda.synchronize()
 
     K = args.steps
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(K)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    graph = dw.capture_step() if args.graph else None
+    graph = dw.capture_step(side_stream=side) if args.launch.startswith("graph") else None
     torch.cuda.synchronize()
     start.record()
     for i in range(K):
         if graph is not None:
             graph.replay()
+            continue
+        if side is not None:
+            dw.mixed_step(side_stream=side)
             continue
         dw.append_step()
         if wl.num_seqs:
@@ -186,9 +199,9 @@ def main() -> int:
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / K
-    if graph is not None:
-        # The kernel's own duration cannot be bracketed inside a replay: time
-        # it in a short eager loop after the replays.
+    if args.launch != "calls":
+        # The kernel's own duration cannot be bracketed inside a replay or a
+        # fused call: time it in a short eager loop after the timed steps.
         for i in range(K):
             dw.append_step()
             if wl.num_seqs:
@@ -232,7 +245,7 @@ def main() -> int:
                    "split_tokens": dw.split_tokens,
                    "prefill_split_tokens": dw.pf["split"] if dw.pf else None,
                    "parallelism": "single GPU",
-                   "launch": "hip graph replay" if args.graph else "eager launches"},
+                   "launch": args.launch},
         "seq_steps_per_s": round(wl.num_seqs / (ms * 1e-3), 1),
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "step_bytes": step_bytes,

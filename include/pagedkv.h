@@ -281,6 +281,83 @@ size_t pkv_prefill_workspace_bytes(const pkv_cache_desc* cache, int32_t num_reqs
                                    int32_t split_tokens);
 
 /* ------------------------------------------------------------------------ *
+ * mixed_step — one in-flight batching step in one call: new tokens join the
+ * cache, then decode sequences and prefill chunks attend it
+ * ("TensorRT-LLM内核融合与动态批处理", In-flight Batching: requests at different
+ * phases share a step; first page §5.3 for the chunks).  The three parts are
+ * the arguments of pkv_kv_cache_append, pkv_paged_attn_decode and
+ * pkv_paged_attn_chunked_prefill gathered in structs; any part may be NULL.
+ *
+ * Order: the append runs on `stream`; decode (partial + merge) and prefill
+ * (+ merge) follow it.  With side_stream non-NULL (and different from
+ * stream) the prefill runs on side_stream concurrently with the decode —
+ * the decode reads HBM while the prefill keeps the matrix cores busy — and
+ * `stream` waits for it before the call's work is complete; the fork and
+ * join are stream events, so a graph captured from `stream` records all of
+ * it.  Both streams belong to the current device.  With side_stream NULL the
+ * parts run one after another on `stream`.
+ *
+ * Every part is checked on the host before anything is launched.  When the
+ * two attention parts run concurrently their workspaces must not overlap
+ * (PKV_ERR_INVALID_ARG).  The library keeps two events per host thread and
+ * device for the fork and join, created on first use and kept until the
+ * process ends; calls from one thread are ordered, calls from several
+ * threads do not share events.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  const void* k_new;
+  const void* v_new;
+  int32_t in_dtype;
+  const int32_t* cu_new_tokens;
+  const int32_t* start_pos;
+  const int32_t* block_tables;
+  int32_t bt_stride;
+  int32_t num_rows;
+  int32_t num_new_tokens;
+} pkv_append_batch;
+
+typedef struct {
+  const void* q;
+  int32_t q_dtype;
+  void* out;
+  int32_t out_dtype;
+  float* lse;
+  const int32_t* block_tables;
+  int32_t bt_stride;
+  const int32_t* context_lens;
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t max_context_len;
+  int32_t split_tokens;
+  void* workspace;
+  size_t workspace_bytes;
+} pkv_decode_batch;
+
+typedef struct {
+  const void* q;
+  int32_t q_dtype;
+  void* out;
+  int32_t out_dtype;
+  float* lse;
+  const int32_t* cu_q_lens;
+  const int32_t* ctx_before;
+  const int32_t* block_tables;
+  int32_t bt_stride;
+  int32_t num_reqs;
+  int32_t num_q_tokens;
+  int32_t num_q_heads;
+  int32_t max_chunk_len;
+  int32_t max_total_len;
+  int32_t split_tokens;
+  void* workspace;
+  size_t workspace_bytes;
+} pkv_prefill_batch;
+
+pkv_status pkv_mixed_step(const pkv_cache_desc* cache, const pkv_append_batch* append,
+                          const pkv_decode_batch* decode, const pkv_prefill_batch* prefill,
+                          float sm_scale, void* stream, void* side_stream);
+
+/* ------------------------------------------------------------------------ *
  * Utilities
  * ------------------------------------------------------------------------ */
 

@@ -10,4 +10,5 @@ from .binding import (PagedCache, PageAllocator, PkvError, decode_workspace, lib
                       pkv_kv_cache_append, pkv_lse_merge, pkv_paged_attn_chunked_prefill,
                       pkv_paged_attn_decode, pkv_paged_attn_decode_partial,
                       pkv_prefill_split_tokens, pkv_prefill_workspace_bytes, prefill_workspace,
-                      pkv_validate_block_tables)
+                      pkv_validate_block_tables, pkv_mixed_step, append_batch,
+                      decode_batch, prefill_batch)

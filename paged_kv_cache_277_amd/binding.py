@@ -43,6 +43,32 @@ class CacheDescStruct(C.Structure):
                 ("page_size", C.c_int32), ("head_dim", C.c_int32), ("kv_dtype", C.c_int32)]
 
 
+class AppendBatchStruct(C.Structure):
+    _fields_ = [("k_new", C.c_void_p), ("v_new", C.c_void_p), ("in_dtype", C.c_int32),
+                ("cu_new_tokens", C.c_void_p), ("start_pos", C.c_void_p),
+                ("block_tables", C.c_void_p), ("bt_stride", C.c_int32), ("num_rows", C.c_int32),
+                ("num_new_tokens", C.c_int32)]
+
+
+class DecodeBatchStruct(C.Structure):
+    _fields_ = [("q", C.c_void_p), ("q_dtype", C.c_int32), ("out", C.c_void_p),
+                ("out_dtype", C.c_int32), ("lse", C.c_void_p), ("block_tables", C.c_void_p),
+                ("bt_stride", C.c_int32), ("context_lens", C.c_void_p), ("num_seqs", C.c_int32),
+                ("num_q_heads", C.c_int32), ("max_context_len", C.c_int32),
+                ("split_tokens", C.c_int32), ("workspace", C.c_void_p),
+                ("workspace_bytes", C.c_size_t)]
+
+
+class PrefillBatchStruct(C.Structure):
+    _fields_ = [("q", C.c_void_p), ("q_dtype", C.c_int32), ("out", C.c_void_p),
+                ("out_dtype", C.c_int32), ("lse", C.c_void_p), ("cu_q_lens", C.c_void_p),
+                ("ctx_before", C.c_void_p), ("block_tables", C.c_void_p),
+                ("bt_stride", C.c_int32), ("num_reqs", C.c_int32), ("num_q_tokens", C.c_int32),
+                ("num_q_heads", C.c_int32), ("max_chunk_len", C.c_int32),
+                ("max_total_len", C.c_int32), ("split_tokens", C.c_int32),
+                ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t)]
+
+
 _P = C.c_void_p
 _I = C.c_int32
 _F = C.c_float
@@ -67,6 +93,7 @@ _SIGS = {
                                             _I, _I, _F, _I, _P, _SZ, _P]),
     "pkv_prefill_split_tokens": (_I, [_P, _I, _I, _I, _I]),
     "pkv_prefill_workspace_bytes": (_SZ, [_P, _I, _I, _I, _I, _I, _I]),
+    "pkv_mixed_step": (_I, [_P, _P, _P, _P, _F, _P, _P]),
     "pkv_validate_block_tables": (_I, [_P, _P, _I, _P, _I, _P]),
     "pkv_fp8_e4m3fn_to_f32": (_I, [_P, _P, C.c_int64, _P]),
 }
@@ -353,6 +380,64 @@ def pkv_paged_attn_chunked_prefill(cache: PagedCache, q: torch.Tensor, out: torc
         cache.desc, _ptr(q), _code_of(q), _ptr(out), _code_of(out), _ptr(lse), _ptr(cu_q_lens),
         _ptr(ctx_before), _ptr(block_tables), block_tables.shape[1], R, q.shape[0], q.shape[1],
         max_chunk_len, max_total_len, float(sm_scale), split_tokens, wp, wb, _stream(stream)))
+
+
+def append_batch(k_new: torch.Tensor, v_new: torch.Tensor, cu_new_tokens: torch.Tensor,
+                 start_pos: torch.Tensor, block_tables: torch.Tensor) -> AppendBatchStruct:
+    """The append part of pkv_mixed_step (tensors as for pkv_kv_cache_append;
+    the caller keeps them alive while the struct is in use)."""
+    for t, n in ((cu_new_tokens, "cu_new_tokens"), (start_pos, "start_pos"),
+                 (block_tables, "block_tables")):
+        _i32(t, n)
+    _need(k_new.shape == v_new.shape and k_new.is_contiguous() and v_new.is_contiguous(),
+          "k_new / v_new must be contiguous [T][Hkv][D]")
+    return AppendBatchStruct(_ptr(k_new), _ptr(v_new), _code_of(k_new), _ptr(cu_new_tokens),
+                             _ptr(start_pos), _ptr(block_tables),
+                             block_tables.shape[1] if block_tables.dim() == 2 else 0,
+                             start_pos.shape[0], k_new.shape[0])
+
+
+def decode_batch(q: torch.Tensor, out: torch.Tensor, block_tables: torch.Tensor,
+                 context_lens: torch.Tensor, max_context_len: int,
+                 lse: Optional[torch.Tensor] = None, split_tokens: int = 0,
+                 workspace: Optional[torch.Tensor] = None) -> DecodeBatchStruct:
+    """The decode part of pkv_mixed_step (arguments as for pkv_paged_attn_decode)."""
+    _decode_args(None, q, out, lse, block_tables, context_lens)
+    wp, wb = _ws(workspace)
+    return DecodeBatchStruct(_ptr(q), _code_of(q), _ptr(out), _code_of(out), _ptr(lse),
+                             _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
+                             q.shape[0], q.shape[1], max_context_len, split_tokens, wp, wb)
+
+
+def prefill_batch(q: torch.Tensor, out: torch.Tensor, cu_q_lens: torch.Tensor,
+                  ctx_before: torch.Tensor, block_tables: torch.Tensor, max_chunk_len: int,
+                  max_total_len: int, lse: Optional[torch.Tensor] = None, split_tokens: int = 0,
+                  workspace: Optional[torch.Tensor] = None) -> PrefillBatchStruct:
+    """The prefill part of pkv_mixed_step (arguments as for
+    pkv_paged_attn_chunked_prefill)."""
+    _need(q.dim() == 3 and q.is_contiguous() and out.shape == q.shape and out.is_contiguous(),
+          "q / out must be contiguous [T][Hq][D]")
+    for t, n in ((cu_q_lens, "cu_q_lens"), (ctx_before, "ctx_before"),
+                 (block_tables, "block_tables")):
+        _i32(t, n)
+    R = ctx_before.shape[0]
+    _need(cu_q_lens.shape[0] == R + 1 and block_tables.shape[0] == R, "request counts differ")
+    wp, wb = _ws(workspace)
+    return PrefillBatchStruct(_ptr(q), _code_of(q), _ptr(out), _code_of(out), _ptr(lse),
+                              _ptr(cu_q_lens), _ptr(ctx_before), _ptr(block_tables),
+                              block_tables.shape[1], R, q.shape[0], q.shape[1], max_chunk_len,
+                              max_total_len, split_tokens, wp, wb)
+
+
+def pkv_mixed_step(cache: PagedCache, append: Optional[AppendBatchStruct],
+                   decode: Optional[DecodeBatchStruct], prefill: Optional[PrefillBatchStruct],
+                   sm_scale: float, stream=None, side_stream=None) -> None:
+    """Append, then decode and prefill (concurrently when side_stream is given)."""
+    side = None if side_stream is None else _stream(side_stream)
+    _check(lib().pkv_mixed_step(cache.desc, None if append is None else C.byref(append),
+                                None if decode is None else C.byref(decode),
+                                None if prefill is None else C.byref(prefill), float(sm_scale),
+                                _stream(stream), side))
 
 
 def pkv_validate_block_tables(cache: PagedCache, block_tables: torch.Tensor, lens: torch.Tensor,

@@ -281,6 +281,132 @@ pkv_status prepare_prefill(const pkv_cache_desc* cache, int32_t q_dtype, int32_t
   return PKV_OK;
 }
 
+pkv_status prepare_append(const pkv_cache_desc* cache, const void* k_new, const void* v_new,
+                          int32_t in_dtype, const int32_t* cu_new_tokens,
+                          const int32_t* start_pos, const int32_t* block_tables,
+                          int32_t bt_stride, int32_t num_rows, int32_t num_new_tokens,
+                          pkv::AppendArgs* a) {
+  pkv_status st;
+  if ((st = check_cache(cache)) != PKV_OK) return st;
+  const int32_t want_in = cache->kv_dtype == PKV_FP8_E4M3FN ? PKV_F32 : cache->kv_dtype;
+  if (in_dtype != want_in)
+    return fail(PKV_ERR_UNSUPPORTED, "append into kv_dtype %d takes in_dtype %d, got %d",
+                cache->kv_dtype, want_in, in_dtype);
+  if (num_rows < 0 || num_new_tokens < 0)
+    return fail(PKV_ERR_INVALID_ARG, "num_rows %d / num_new_tokens %d negative", num_rows,
+                num_new_tokens);
+  if (num_new_tokens > 0) {
+    if (num_rows == 0) return fail(PKV_ERR_INVALID_ARG, "tokens given but no rows");
+    if (!k_new || !v_new || !cu_new_tokens || !start_pos || !block_tables)
+      return fail(PKV_ERR_INVALID_ARG, "append pointers must not be NULL");
+    if (bt_stride <= 0) return fail(PKV_ERR_INVALID_ARG, "bt_stride %d", bt_stride);
+  }
+  std::memset(a, 0, sizeof *a);
+  a->c = view(cache);
+  a->k_new = k_new;
+  a->v_new = v_new;
+  a->in_dtype = in_dtype;
+  a->cu = cu_new_tokens;
+  a->start_pos = start_pos;
+  a->bt = block_tables;
+  a->bt_stride = bt_stride;
+  a->num_rows = num_rows;
+  a->num_tokens = num_new_tokens;
+  return PKV_OK;
+}
+
+// All host checks of a prefill call; on success `a` is ready to launch and
+// *need holds the workspace bytes it uses.
+pkv_status prepare_prefill_call(const pkv_cache_desc* cache, const void* q, int32_t q_dtype,
+                                void* out, int32_t out_dtype, float* lse,
+                                const int32_t* cu_q_lens, const int32_t* ctx_before,
+                                const int32_t* block_tables, int32_t bt_stride, int32_t num_reqs,
+                                int32_t num_q_tokens, int32_t num_q_heads, int32_t max_chunk_len,
+                                int32_t max_total_len, float sm_scale, int32_t split_tokens,
+                                void* workspace, size_t workspace_bytes_in, pkv::AttnArgs* a,
+                                size_t* need_out = nullptr) {
+  pkv_status st = prepare_prefill(cache, q_dtype, out_dtype, num_reqs, num_q_tokens, num_q_heads,
+                                  max_chunk_len, max_total_len, split_tokens, a);
+  if (st != PKV_OK) return st;
+  if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f))
+    return fail(PKV_ERR_INVALID_ARG, "sm_scale must be finite and positive");
+  if (need_out) *need_out = 0;
+  if (num_q_tokens == 0 || num_reqs == 0) return PKV_OK;
+  if (!q || !out || !cu_q_lens || !ctx_before || !block_tables)
+    return fail(PKV_ERR_INVALID_ARG, "prefill pointers must not be NULL");
+  if (bt_stride <= 0) return fail(PKV_ERR_INVALID_ARG, "bt_stride %d", bt_stride);
+  if ((int64_t)bt_stride * cache->page_size < max_total_len)
+    return fail(PKV_ERR_INVALID_ARG, "max_total_len %d exceeds bt_stride*page_size %lld",
+                max_total_len, (long long)bt_stride * cache->page_size);
+  const size_t need = prefill_ws_bytes(cache, num_q_tokens, num_q_heads, a->max_splits);
+  if (need > 0 && (!workspace || workspace_bytes_in < need))
+    return fail(PKV_ERR_INVALID_ARG, "workspace of %zu bytes needed, %zu given", need,
+                workspace_bytes_in);
+  a->q = q;
+  a->out = out;
+  a->lse = lse;
+  a->bt = block_tables;
+  a->bt_stride = bt_stride;
+  a->cu_q = cu_q_lens;
+  a->ctx_before = ctx_before;
+  a->sm_scale = sm_scale;
+  if (need > 0) {
+    char* w = static_cast<char*>(workspace);
+    const size_t n = (size_t)num_q_tokens * num_q_heads * a->max_splits;
+    a->ws_acc = reinterpret_cast<float*>(w);
+    a->ws_ml = reinterpret_cast<float*>(w + (n * cache->head_dim * 4 + 255) / 256 * 256);
+  }
+  if (need_out) *need_out = need;
+  return PKV_OK;
+}
+
+pkv_status launch_prefill_call(const pkv::AttnArgs& a, hipStream_t s) {
+  if (a.num_rows == 0 || a.num_tokens == 0) return PKV_OK;
+  pkv_status st;
+  if ((st = hip_status(pkv::launch_prefill(a, s), "paged_attn_chunked_prefill")) != PKV_OK)
+    return st;
+  return hip_status(pkv::launch_lse_merge(a, s), "paged_attn_chunked_prefill (merge)");
+}
+
+pkv_status launch_decode_call(const pkv::AttnArgs& a, hipStream_t s) {
+  pkv_status st;
+  if ((st = hip_status(pkv::launch_decode_partial(a, s), "paged_attn_decode (partial)")) != PKV_OK)
+    return st;
+  return hip_status(pkv::launch_lse_merge(a, s), "paged_attn_decode (merge)");
+}
+
+// Fork / join events of pkv_mixed_step, one pair per host thread and device
+// (a thread issues one call at a time, so its pair is never shared).  They
+// live until the process ends.
+pkv_status step_events(hipEvent_t* fork, hipEvent_t* join) {
+  struct Pair { int dev; hipEvent_t f, j; };
+  thread_local std::vector<Pair> pairs;
+  int dev = 0;
+  pkv_status st;
+  if ((st = hip_status(hipGetDevice(&dev), "mixed_step: current device")) != PKV_OK) return st;
+  for (const Pair& p : pairs)
+    if (p.dev == dev) { *fork = p.f; *join = p.j; return PKV_OK; }
+  Pair p{dev, nullptr, nullptr};
+  if ((st = hip_status(hipEventCreateWithFlags(&p.f, hipEventDisableTiming),
+                       "mixed_step: create event")) != PKV_OK)
+    return st;
+  if ((st = hip_status(hipEventCreateWithFlags(&p.j, hipEventDisableTiming),
+                       "mixed_step: create event")) != PKV_OK) {
+    (void)hipEventDestroy(p.f);
+    return st;
+  }
+  pairs.push_back(p);
+  *fork = p.f;
+  *join = p.j;
+  return PKV_OK;
+}
+
+bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
 }  // namespace
 
 namespace pkv_detail {
@@ -298,32 +424,10 @@ pkv_status pkv_kv_cache_append(const pkv_cache_desc* cache, const void* k_new, c
                                const int32_t* start_pos, const int32_t* block_tables,
                                int32_t bt_stride, int32_t num_rows, int32_t num_new_tokens,
                                void* stream) {
-  pkv_status st;
-  if ((st = check_cache(cache)) != PKV_OK) return st;
-  const int32_t want_in = cache->kv_dtype == PKV_FP8_E4M3FN ? PKV_F32 : cache->kv_dtype;
-  if (in_dtype != want_in)
-    return fail(PKV_ERR_UNSUPPORTED, "append into kv_dtype %d takes in_dtype %d, got %d",
-                cache->kv_dtype, want_in, in_dtype);
-  if (num_rows < 0 || num_new_tokens < 0)
-    return fail(PKV_ERR_INVALID_ARG, "num_rows %d / num_new_tokens %d negative", num_rows,
-                num_new_tokens);
-  if (num_new_tokens > 0) {
-    if (num_rows == 0) return fail(PKV_ERR_INVALID_ARG, "tokens given but no rows");
-    if (!k_new || !v_new || !cu_new_tokens || !start_pos || !block_tables)
-      return fail(PKV_ERR_INVALID_ARG, "append pointers must not be NULL");
-    if (bt_stride <= 0) return fail(PKV_ERR_INVALID_ARG, "bt_stride %d", bt_stride);
-  }
   pkv::AppendArgs a;
-  a.c = view(cache);
-  a.k_new = k_new;
-  a.v_new = v_new;
-  a.in_dtype = in_dtype;
-  a.cu = cu_new_tokens;
-  a.start_pos = start_pos;
-  a.bt = block_tables;
-  a.bt_stride = bt_stride;
-  a.num_rows = num_rows;
-  a.num_tokens = num_new_tokens;
+  pkv_status st = prepare_append(cache, k_new, v_new, in_dtype, cu_new_tokens, start_pos,
+                                 block_tables, bt_stride, num_rows, num_new_tokens, &a);
+  if (st != PKV_OK) return st;
   return hip_status(pkv::launch_append(a, static_cast<hipStream_t>(stream)), "kv_cache_append");
 }
 
@@ -385,10 +489,7 @@ pkv_status pkv_paged_attn_decode(const pkv_cache_desc* cache, const void* q, int
                                  context_lens, num_seqs, num_q_heads, max_context_len, sm_scale,
                                  split_tokens, workspace, workspace_bytes_in, true, &a);
   if (st != PKV_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if ((st = hip_status(pkv::launch_decode_partial(a, s), "paged_attn_decode (partial)")) != PKV_OK)
-    return st;
-  return hip_status(pkv::launch_lse_merge(a, s), "paged_attn_decode (merge)");
+  return launch_decode_call(a, static_cast<hipStream_t>(stream));
 }
 
 pkv_status pkv_paged_attn_chunked_prefill(const pkv_cache_desc* cache, const void* q,
@@ -401,40 +502,12 @@ pkv_status pkv_paged_attn_chunked_prefill(const pkv_cache_desc* cache, const voi
                                           float sm_scale, int32_t split_tokens, void* workspace,
                                           size_t workspace_bytes_in, void* stream) {
   pkv::AttnArgs a;
-  pkv_status st = prepare_prefill(cache, q_dtype, out_dtype, num_reqs, num_q_tokens, num_q_heads,
-                                  max_chunk_len, max_total_len, split_tokens, &a);
+  pkv_status st = prepare_prefill_call(cache, q, q_dtype, out, out_dtype, lse, cu_q_lens,
+                                       ctx_before, block_tables, bt_stride, num_reqs,
+                                       num_q_tokens, num_q_heads, max_chunk_len, max_total_len,
+                                       sm_scale, split_tokens, workspace, workspace_bytes_in, &a);
   if (st != PKV_OK) return st;
-  if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f))
-    return fail(PKV_ERR_INVALID_ARG, "sm_scale must be finite and positive");
-  if (num_q_tokens == 0 || num_reqs == 0) return PKV_OK;
-  if (!q || !out || !cu_q_lens || !ctx_before || !block_tables)
-    return fail(PKV_ERR_INVALID_ARG, "prefill pointers must not be NULL");
-  if (bt_stride <= 0) return fail(PKV_ERR_INVALID_ARG, "bt_stride %d", bt_stride);
-  if ((int64_t)bt_stride * cache->page_size < max_total_len)
-    return fail(PKV_ERR_INVALID_ARG, "max_total_len %d exceeds bt_stride*page_size %lld",
-                max_total_len, (long long)bt_stride * cache->page_size);
-  const size_t need = prefill_ws_bytes(cache, num_q_tokens, num_q_heads, a.max_splits);
-  if (need > 0 && (!workspace || workspace_bytes_in < need))
-    return fail(PKV_ERR_INVALID_ARG, "workspace of %zu bytes needed, %zu given", need,
-                workspace_bytes_in);
-  a.q = q;
-  a.out = out;
-  a.lse = lse;
-  a.bt = block_tables;
-  a.bt_stride = bt_stride;
-  a.cu_q = cu_q_lens;
-  a.ctx_before = ctx_before;
-  a.sm_scale = sm_scale;
-  if (need > 0) {
-    char* w = static_cast<char*>(workspace);
-    const size_t n = (size_t)num_q_tokens * num_q_heads * a.max_splits;
-    a.ws_acc = reinterpret_cast<float*>(w);
-    a.ws_ml = reinterpret_cast<float*>(w + (n * cache->head_dim * 4 + 255) / 256 * 256);
-  }
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if ((st = hip_status(pkv::launch_prefill(a, s), "paged_attn_chunked_prefill")) != PKV_OK)
-    return st;
-  return hip_status(pkv::launch_lse_merge(a, s), "paged_attn_chunked_prefill (merge)");
+  return launch_prefill_call(a, static_cast<hipStream_t>(stream));
 }
 
 int32_t pkv_prefill_split_tokens(const pkv_cache_desc* cache, int32_t num_reqs,
@@ -455,6 +528,54 @@ size_t pkv_prefill_workspace_bytes(const pkv_cache_desc* cache, int32_t num_reqs
                       max_total_len, split_tokens, &a) != PKV_OK)
     return 0;
   return prefill_ws_bytes(cache, num_q_tokens, num_q_heads, a.max_splits);
+}
+
+pkv_status pkv_mixed_step(const pkv_cache_desc* cache, const pkv_append_batch* ap,
+                          const pkv_decode_batch* dp, const pkv_prefill_batch* pp,
+                          float sm_scale, void* stream, void* side_stream) {
+  pkv::AppendArgs aa;
+  pkv::AttnArgs da, pa;
+  pkv_status st;
+  if (ap && (st = prepare_append(cache, ap->k_new, ap->v_new, ap->in_dtype, ap->cu_new_tokens,
+                                 ap->start_pos, ap->block_tables, ap->bt_stride, ap->num_rows,
+                                 ap->num_new_tokens, &aa)) != PKV_OK)
+    return st;
+  size_t dneed = 0, pneed = 0;
+  if (dp) {
+    if ((st = prepare_decode(cache, dp->q, dp->q_dtype, dp->out, dp->out_dtype, dp->lse,
+                             dp->block_tables, dp->bt_stride, dp->context_lens, dp->num_seqs,
+                             dp->num_q_heads, dp->max_context_len, sm_scale, dp->split_tokens,
+                             dp->workspace, dp->workspace_bytes, true, &da)) != PKV_OK)
+      return st;
+    dneed = workspace_bytes(cache, dp->num_seqs, dp->num_q_heads, dp->max_context_len,
+                            da.split_tokens);
+  }
+  if (pp && (st = prepare_prefill_call(cache, pp->q, pp->q_dtype, pp->out, pp->out_dtype,
+                                       pp->lse, pp->cu_q_lens, pp->ctx_before, pp->block_tables,
+                                       pp->bt_stride, pp->num_reqs, pp->num_q_tokens,
+                                       pp->num_q_heads, pp->max_chunk_len, pp->max_total_len,
+                                       sm_scale, pp->split_tokens, pp->workspace,
+                                       pp->workspace_bytes, &pa, &pneed)) != PKV_OK)
+    return st;
+  if (dp && pp && side_stream && ranges_overlap(dp->workspace, dneed, pp->workspace, pneed))
+    return fail(PKV_ERR_INVALID_ARG, "decode and prefill workspaces overlap (they run concurrently)");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipStream_t side = static_cast<hipStream_t>(side_stream);
+  if (ap && (st = hip_status(pkv::launch_append(aa, s), "mixed_step: append")) != PKV_OK) return st;
+  const bool fork = dp && pp && side && side != s;
+  if (!fork) {
+    if (pp && (st = launch_prefill_call(pa, s)) != PKV_OK) return st;
+    if (dp && (st = launch_decode_call(da, s)) != PKV_OK) return st;
+    return PKV_OK;
+  }
+  hipEvent_t ev_fork, ev_join;
+  if ((st = step_events(&ev_fork, &ev_join)) != PKV_OK) return st;
+  if ((st = hip_status(hipEventRecord(ev_fork, s), "mixed_step: fork")) != PKV_OK) return st;
+  if ((st = hip_status(hipStreamWaitEvent(side, ev_fork, 0), "mixed_step: fork")) != PKV_OK) return st;
+  if ((st = launch_prefill_call(pa, side)) != PKV_OK) return st;   // longer branch first
+  if ((st = launch_decode_call(da, s)) != PKV_OK) return st;
+  if ((st = hip_status(hipEventRecord(ev_join, side), "mixed_step: join")) != PKV_OK) return st;
+  return hip_status(hipStreamWaitEvent(s, ev_join, 0), "mixed_step: join");
 }
 
 pkv_status pkv_validate_block_tables(const pkv_cache_desc* cache, const int32_t* block_tables,

@@ -72,6 +72,7 @@ class DeviceWorkload:
     split_tokens: int
     workspace: Optional[torch.Tensor]
     pf: dict = field(default_factory=dict)
+    _batches: Optional[tuple] = None
 
     def setup(self, stream=None) -> None:
         self._append(self.setup_batch, stream)
@@ -117,24 +118,48 @@ class DeviceWorkload:
         self.decode(stream)
         self.prefill(stream)
 
-    def capture_step(self) -> "torch.cuda.CUDAGraph":
-        """Record one step (every launch of `step`) as a HIP graph.
+    def mixed_step(self, stream=None, side_stream=None) -> None:
+        """The same step in one library call; with side_stream the prefill
+        runs concurrently with the decode."""
+        if self._batches is None:
+            p = self.pf
+            a = self.step_batch
+            self._batches = (
+                B.append_batch(a.k, a.v, a.cu, a.start, a.bt) if a.rows else None,
+                B.decode_batch(self.q, self.out, self.bt, self.lens, self.max_len, lse=self.lse,
+                               split_tokens=self.split_tokens, workspace=self.workspace)
+                if self.wl.num_seqs else None,
+                B.prefill_batch(p["q"], p["out"], p["cu"], p["ctx"], p["bt"], p["max_chunk"],
+                                p["max_total"], lse=p["lse"], split_tokens=p["split"],
+                                workspace=p["ws"]) if p else None)
+        B.pkv_mixed_step(self.cache, *self._batches, float(self.wl.sm_scale), stream=stream,
+                         side_stream=side_stream)
 
-        The library launches only kernels on the caller's stream and allocates
-        nothing, so stream capture records the whole step; replaying the graph
-        re-runs the same kernels on the same buffers with one launch.  (A CUDA
-        graph captured per batch shape is the pages' own remedy for launch
-        overhead in small decode steps: "TensorRT-LLM框架解析与高性能推理优化实践"
-        §8.1.)"""
+    def capture_step(self, side_stream=None) -> "torch.cuda.CUDAGraph":
+        """Record one step as a HIP graph.
+
+        The library launches only kernels on the caller's streams and
+        allocates nothing, so stream capture records the whole step; replaying
+        the graph re-runs the same kernels on the same buffers with one launch.
+        With side_stream the step is the one-call mixed step whose prefill
+        branch forks onto side_stream (the fork and join are captured too).
+        (A CUDA graph captured per batch shape is the pages' own remedy for
+        launch overhead in small decode steps:
+        "TensorRT-LLM框架解析与高性能推理优化实践" §8.1.)"""
+        def run():
+            if side_stream is None:
+                self.step()
+            else:
+                self.mixed_step(side_stream=side_stream)
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):          # warm the capture stream once
-            self.step()
+            run()
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            self.step()
+            run()
         torch.cuda.synchronize()
         return g
 

@@ -232,3 +232,29 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "_lib", None)
     with pytest.raises(ImportError, match="no fallback"):
         B.lib()
+
+
+def test_mixed_step_checks_every_part_before_launching():
+    lib = B.lib()
+    d = _desc(num_pages=64)
+    # nothing to do
+    assert lib.pkv_mixed_step(C.byref(d), None, None, None, 0.1, None, None) == B.PKV_OK
+    app = B.AppendBatchStruct(FAKE, FAKE, B.PKV_BF16, FAKE, FAKE, FAKE, 4, 1, 1)
+    good_dec = B.DecodeBatchStruct(FAKE, B.PKV_BF16, FAKE, B.PKV_BF16, None, FAKE, 4, FAKE, 2, 4,
+                                   64, 32, FAKE, 1 << 20)
+    bad_dec = B.DecodeBatchStruct(FAKE, B.PKV_BF16, FAKE, B.PKV_BF16, None, FAKE, 4, FAKE, 2, 3,
+                                  64, 0, None, 0)                                   # Hq 3
+    pre = B.PrefillBatchStruct(FAKE, B.PKV_BF16, FAKE, B.PKV_BF16, None, FAKE, FAKE, FAKE, 8, 2, 8,
+                               4, 4, 128, 64, FAKE + 4096, 1 << 20)
+    # a bad decode part fails its host check: the (valid) append part was not
+    # launched, which on a machine without a GPU would have returned PKV_ERR_HIP
+    assert lib.pkv_mixed_step(C.byref(d), C.byref(app), C.byref(bad_dec), None, 0.1, None,
+                              None) == B.PKV_ERR_INVALID_ARG
+    # concurrent decode and prefill may not share workspace bytes
+    assert lib.pkv_mixed_step(C.byref(d), None, C.byref(good_dec), C.byref(pre), 0.1, None,
+                              FAKE) == B.PKV_ERR_INVALID_ARG
+    assert b"overlap" in lib.pkv_last_error()
+    bad_pre = B.PrefillBatchStruct(FAKE, B.PKV_BF16, FAKE, B.PKV_BF16, None, FAKE, FAKE, FAKE, 8,
+                                   2, 8, 4, 4, 3, 0, None, 0)               # total < chunk
+    assert lib.pkv_mixed_step(C.byref(d), C.byref(app), C.byref(good_dec), C.byref(bad_pre), 0.1,
+                              None, None) == B.PKV_ERR_INVALID_ARG

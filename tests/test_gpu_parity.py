@@ -376,3 +376,43 @@ def test_step_graph_replays_match_eager(cfg):
     kp, vp = sup.oracle_pools(wl)
     ref, _ = sup.oracle_decode(wl, kp, vp)
     check_close(dw.out, ref, wl.spec)
+
+
+@pytest.mark.parametrize("cfg", [1, 5])
+def test_mixed_step_call_and_overlapped_graph_match_eager(cfg):
+    """pkv_mixed_step with the prefill forked onto a second stream, called
+    directly and replayed from a captured graph, gives the eager step's bits."""
+    wl = wk.make_workload(wk.CONFIGS[cfg]) if cfg == 1 else wk.make_workload(
+        spec_of((40, 300, 1000), 32, 8, 128, 32, "bf16", prefill_ctx=(0, 100, 700),
+                prefill_chunk=70), seed=6)
+    dw = dev.upload(wl, prefill_split=64)
+    dw.setup()
+    dw.step()
+    torch.cuda.synchronize()
+    ref = [dw.out.clone(), dw.lse.clone()] + ([dw.pf["out"].clone(), dw.pf["lse"].clone()]
+                                              if dw.pf else [])
+
+    def outs():
+        return [dw.out, dw.lse] + ([dw.pf["out"], dw.pf["lse"]] if dw.pf else [])
+
+    def clear():
+        for t in outs():
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+
+    side = torch.cuda.Stream()
+    for rep in range(2):
+        clear()
+        dw.mixed_step(side_stream=side)
+        torch.cuda.synchronize()
+        for a, b in zip(outs(), ref):
+            assert torch.equal(a, b), f"mixed_step call {rep} differs from the eager step"
+    g = dw.capture_step(side_stream=side)
+    for rep in range(3):
+        clear()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outs(), ref):
+            assert torch.equal(a, b), f"graph replay {rep} differs from the eager step"
+        dw.step()                                   # eager work between replays
+        torch.cuda.synchronize()
