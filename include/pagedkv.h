@@ -358,6 +358,98 @@ pkv_status pkv_mixed_step(const pkv_cache_desc* cache, const pkv_append_batch* a
                           float sm_scale, void* stream, void* side_stream);
 
 /* ------------------------------------------------------------------------ *
+ * Step scheduler with the KV-cache manager — host only, produces the block
+ * tables and positions the kernels above consume
+ * ("TensorRT-LLM框架解析与高性能推理优化实践" §4.2 KVCacheManager, §5.1
+ * capacity / micro-batch scheduling, §5.2 LIFO preemption, §5.3 chunked
+ * context, §4.1 slot manager).
+ *
+ * Per request: num_tokens = prompt + generated tokens, num_computed = tokens
+ * with K/V in the cache.  pkv_sched_schedule plans one step:
+ *   1. running requests, oldest admitted first, each computing its next
+ *      prefill chunk (min(chunk_size, num_tokens - num_computed)) or, with
+ *      one token pending, one decode token, within max_num_tokens per step.
+ *      A request short of pages evicts the most recently admitted running
+ *      request (possibly itself): its pages are freed and it returns to the
+ *      front of the waiting queue, to be recomputed from its prefix on resume.
+ *   2. waiting requests from the front, while they fit (max_batch_size
+ *      running, the token budget, and pages: the next chunk's pages in the
+ *      aggressive policy; every running request's remaining worst case plus
+ *      the new one's in the conservative policy, which therefore never
+ *      evicts).  Admission never evicts and never skips the queue front.
+ * pkv_sched_commit then records the step as executed: num_computed advances,
+ * a request whose cache caught up with num_tokens gains one generated token,
+ * and one with max_new_tokens generated finishes (pages freed).
+ *
+ * A request whose worst case (prompt + max_new_tokens - 1 cached tokens)
+ * cannot fit the pool beside the registered prefixes is refused with
+ * PKV_ERR_OUT_OF_PAGES at pkv_sched_add_request.  Shared prefixes are whole
+ * pages registered once (the caller fills their K/V); requests naming one
+ * start with those pages (refcounted) and num_computed = the prefix length.
+ * All functions are thread-safe (one mutex per scheduler).
+ * ------------------------------------------------------------------------ */
+typedef enum { PKV_SCHED_CONSERVATIVE = 0, PKV_SCHED_AGGRESSIVE = 1 } pkv_sched_policy;
+typedef enum { PKV_WORK_PREFILL = 0, PKV_WORK_DECODE = 1 } pkv_work_kind;
+
+typedef struct {
+  int32_t num_pages;        /* cache pages managed */
+  int32_t page_size;        /* tokens per page */
+  int32_t max_batch_size;   /* running requests (compute slots) */
+  int32_t max_num_tokens;   /* tokens computed per step, decode + prefill */
+  int32_t chunk_size;       /* prefill tokens per request per step */
+  int32_t policy;           /* pkv_sched_policy */
+} pkv_sched_config;
+
+typedef struct {
+  int64_t req_id;
+  int32_t slot;             /* compute slot, 0 .. max_batch_size-1 */
+  int32_t kind;             /* pkv_work_kind */
+  int32_t start_pos;        /* tokens already cached (= append start_pos) */
+  int32_t num_tokens;       /* tokens appended and attended this step */
+} pkv_sched_item;
+
+typedef struct {
+  int32_t num_tokens, num_computed, generated, num_pages, slot, running;
+} pkv_sched_request_state;
+
+typedef struct {
+  int32_t waiting, running, free_pages;
+  int64_t preemptions;      /* evictions since creation */
+} pkv_sched_counts;
+
+pkv_status pkv_sched_create(const pkv_sched_config* cfg, void** out_sched);
+void       pkv_sched_destroy(void* sched);
+/* Registers num_tokens (a positive multiple of page_size) of shared prefix;
+ * out_pages receives its num_tokens / page_size page ids. */
+pkv_status pkv_sched_add_prefix(void* sched, int64_t prefix_id, int32_t num_tokens,
+                                int32_t* out_pages);
+/* Fails while a request references the prefix. */
+pkv_status pkv_sched_remove_prefix(void* sched, int64_t prefix_id);
+/* Queues a request at the back of the waiting queue; prefix_id -1 = none
+ * (else prompt_len counts the prefix and must exceed it). */
+pkv_status pkv_sched_add_request(void* sched, int64_t req_id, int32_t prompt_len,
+                                 int32_t max_new_tokens, int64_t prefix_id);
+/* Plans one step into items[] (capacity >= max_batch_size) and lists the
+ * requests evicted by it in preempted[] (capacity >= max_batch_size).
+ * Must be followed by pkv_sched_commit before the next call.
+ * PKV_ERR_OUT_OF_PAGES (nothing planned) when the queue front cannot be
+ * admitted even into an empty batch. */
+pkv_status pkv_sched_schedule(void* sched, pkv_sched_item* items, int32_t items_cap,
+                              int32_t* num_items, int64_t* preempted, int32_t preempted_cap,
+                              int32_t* num_preempted);
+/* Copies up to cap page ids of the request's block table into out (may be
+ * NULL) and returns its page count, or -1 for an unknown request. */
+int32_t    pkv_sched_block_table(const void* sched, int64_t req_id, int32_t* out, int32_t cap);
+/* Records the planned step as executed; finished[] (capacity >= items of the
+ * step) receives the requests that completed and were removed. */
+pkv_status pkv_sched_commit(void* sched, int64_t* finished, int32_t finished_cap,
+                            int32_t* num_finished);
+/* Removes a request early (stop token, cancellation) and frees its pages. */
+pkv_status pkv_sched_finish(void* sched, int64_t req_id);
+pkv_status pkv_sched_query(const void* sched, int64_t req_id, pkv_sched_request_state* out);
+pkv_status pkv_sched_stats(const void* sched, pkv_sched_counts* out);
+
+/* ------------------------------------------------------------------------ *
  * Utilities
  * ------------------------------------------------------------------------ */
 

@@ -5,7 +5,7 @@ ABI of ``include/pagedkv.h``); ``binding`` is its ctypes binding, with the
 same function names as the C entry points.  ``workloads`` draws seeded
 synthetic inputs and ``device`` uploads them and runs one step of the hot path.
 """
-from .binding import (PagedCache, PageAllocator, PkvError, decode_workspace, lib, version,  # noqa: F401
+from .binding import (PagedCache, PageAllocator, PkvError, Scheduler, decode_workspace, lib, version,  # noqa: F401
                       pkv_decode_split_tokens, pkv_decode_workspace_bytes, pkv_fp8_e4m3fn_to_f32,
                       pkv_kv_cache_append, pkv_lse_merge, pkv_paged_attn_chunked_prefill,
                       pkv_paged_attn_decode, pkv_paged_attn_decode_partial,

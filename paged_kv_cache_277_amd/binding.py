@@ -69,6 +69,28 @@ class PrefillBatchStruct(C.Structure):
                 ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t)]
 
 
+class SchedConfigStruct(C.Structure):
+    _fields_ = [("num_pages", C.c_int32), ("page_size", C.c_int32),
+                ("max_batch_size", C.c_int32), ("max_num_tokens", C.c_int32),
+                ("chunk_size", C.c_int32), ("policy", C.c_int32)]
+
+
+class SchedItemStruct(C.Structure):
+    _fields_ = [("req_id", C.c_int64), ("slot", C.c_int32), ("kind", C.c_int32),
+                ("start_pos", C.c_int32), ("num_tokens", C.c_int32)]
+
+
+class SchedRequestStateStruct(C.Structure):
+    _fields_ = [("num_tokens", C.c_int32), ("num_computed", C.c_int32),
+                ("generated", C.c_int32), ("num_pages", C.c_int32), ("slot", C.c_int32),
+                ("running", C.c_int32)]
+
+
+class SchedCountsStruct(C.Structure):
+    _fields_ = [("waiting", C.c_int32), ("running", C.c_int32), ("free_pages", C.c_int32),
+                ("preemptions", C.c_int64)]
+
+
 _P = C.c_void_p
 _I = C.c_int32
 _F = C.c_float
@@ -95,6 +117,17 @@ _SIGS = {
     "pkv_prefill_workspace_bytes": (_SZ, [_P, _I, _I, _I, _I, _I, _I]),
     "pkv_mixed_step": (_I, [_P, _P, _P, _P, _F, _P, _P]),
     "pkv_validate_block_tables": (_I, [_P, _P, _I, _P, _I, _P]),
+    "pkv_sched_create": (_I, [_P, C.POINTER(C.c_void_p)]),
+    "pkv_sched_destroy": (None, [_P]),
+    "pkv_sched_add_prefix": (_I, [_P, C.c_int64, _I, _P]),
+    "pkv_sched_remove_prefix": (_I, [_P, C.c_int64]),
+    "pkv_sched_add_request": (_I, [_P, C.c_int64, _I, _I, C.c_int64]),
+    "pkv_sched_schedule": (_I, [_P, _P, _I, _P, _P, _I, _P]),
+    "pkv_sched_block_table": (_I, [_P, C.c_int64, _P, _I]),
+    "pkv_sched_commit": (_I, [_P, _P, _I, _P]),
+    "pkv_sched_finish": (_I, [_P, C.c_int64]),
+    "pkv_sched_query": (_I, [_P, C.c_int64, _P]),
+    "pkv_sched_stats": (_I, [_P, _P]),
     "pkv_fp8_e4m3fn_to_f32": (_I, [_P, _P, C.c_int64, _P]),
 }
 EXPORTED = tuple(_SIGS)
@@ -198,6 +231,84 @@ class PagedCache:
 
 
 # ---------------------------------------------------------- allocator -------
+PKV_SCHED_CONSERVATIVE, PKV_SCHED_AGGRESSIVE = 0, 1
+PKV_WORK_PREFILL, PKV_WORK_DECODE = 0, 1
+
+
+class Scheduler:
+    """Host step scheduler with its KV-cache page manager (pkv_sched_*).
+
+    schedule() returns ([(req_id, slot, kind, start_pos, num_tokens)], [evicted
+    req_ids]); commit() records the step as executed and returns the finished
+    req_ids."""
+
+    def __init__(self, num_pages: int, page_size: int, max_batch_size: int,
+                 max_num_tokens: int, chunk_size: int, policy: int = PKV_SCHED_AGGRESSIVE):
+        cfg = SchedConfigStruct(num_pages, page_size, max_batch_size, max_num_tokens, chunk_size,
+                                policy)
+        h = C.c_void_p()
+        _check(lib().pkv_sched_create(C.byref(cfg), C.byref(h)))
+        self._h = h
+        self.page_size = page_size
+        self.max_batch_size = max_batch_size
+        self._items = (SchedItemStruct * max_batch_size)()
+        self._ids = (C.c_int64 * max_batch_size)()
+        self._n = C.c_int32()
+        self._m = C.c_int32()
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and _lib is not None:
+            _lib.pkv_sched_destroy(h)
+            self._h = None
+
+    def add_prefix(self, prefix_id: int, num_tokens: int) -> list:
+        out = (C.c_int32 * max(1, num_tokens // self.page_size))()
+        _check(lib().pkv_sched_add_prefix(self._h, prefix_id, num_tokens, out))
+        return list(out)[: num_tokens // self.page_size]
+
+    def remove_prefix(self, prefix_id: int) -> None:
+        _check(lib().pkv_sched_remove_prefix(self._h, prefix_id))
+
+    def add_request(self, req_id: int, prompt_len: int, max_new_tokens: int,
+                    prefix_id: int = -1) -> None:
+        _check(lib().pkv_sched_add_request(self._h, req_id, prompt_len, max_new_tokens,
+                                           prefix_id))
+
+    def schedule(self):
+        _check(lib().pkv_sched_schedule(self._h, self._items, self.max_batch_size,
+                                        C.byref(self._n), self._ids, self.max_batch_size,
+                                        C.byref(self._m)))
+        items = [(it.req_id, it.slot, it.kind, it.start_pos, it.num_tokens)
+                 for it in self._items[: self._n.value]]
+        return items, list(self._ids[: self._m.value])
+
+    def block_table(self, req_id: int) -> list:
+        n = lib().pkv_sched_block_table(self._h, req_id, None, 0)
+        _need(n >= 0, f"unknown request {req_id}")
+        out = (C.c_int32 * max(1, n))()
+        lib().pkv_sched_block_table(self._h, req_id, out, n)
+        return list(out)[:n]
+
+    def commit(self) -> list:
+        _check(lib().pkv_sched_commit(self._h, self._ids, self.max_batch_size,
+                                      C.byref(self._n)))
+        return list(self._ids[: self._n.value])
+
+    def finish(self, req_id: int) -> None:
+        _check(lib().pkv_sched_finish(self._h, req_id))
+
+    def query(self, req_id: int) -> dict:
+        st = SchedRequestStateStruct()
+        _check(lib().pkv_sched_query(self._h, req_id, C.byref(st)))
+        return {k: getattr(st, k) for k, _ in st._fields_}
+
+    def stats(self) -> dict:
+        st = SchedCountsStruct()
+        _check(lib().pkv_sched_stats(self._h, C.byref(st)))
+        return {k: getattr(st, k) for k, _ in st._fields_}
+
+
 class PageAllocator:
     """Host page allocator (refcounted; all-or-nothing allocation)."""
 
@@ -384,17 +495,22 @@ def pkv_paged_attn_chunked_prefill(cache: PagedCache, q: torch.Tensor, out: torc
 
 def append_batch(k_new: torch.Tensor, v_new: torch.Tensor, cu_new_tokens: torch.Tensor,
                  start_pos: torch.Tensor, block_tables: torch.Tensor) -> AppendBatchStruct:
-    """The append part of pkv_mixed_step (tensors as for pkv_kv_cache_append;
-    the caller keeps them alive while the struct is in use)."""
+    """The append part of pkv_mixed_step (tensors as for pkv_kv_cache_append).
+
+    The struct carries raw device pointers; it also holds references to the
+    tensors so their memory stays allocated for as long as the struct lives
+    (the batch helpers below do the same)."""
     for t, n in ((cu_new_tokens, "cu_new_tokens"), (start_pos, "start_pos"),
                  (block_tables, "block_tables")):
         _i32(t, n)
     _need(k_new.shape == v_new.shape and k_new.is_contiguous() and v_new.is_contiguous(),
           "k_new / v_new must be contiguous [T][Hkv][D]")
-    return AppendBatchStruct(_ptr(k_new), _ptr(v_new), _code_of(k_new), _ptr(cu_new_tokens),
-                             _ptr(start_pos), _ptr(block_tables),
-                             block_tables.shape[1] if block_tables.dim() == 2 else 0,
-                             start_pos.shape[0], k_new.shape[0])
+    b = AppendBatchStruct(_ptr(k_new), _ptr(v_new), _code_of(k_new), _ptr(cu_new_tokens),
+                          _ptr(start_pos), _ptr(block_tables),
+                          block_tables.shape[1] if block_tables.dim() == 2 else 0,
+                          start_pos.shape[0], k_new.shape[0])
+    b._tensors = (k_new, v_new, cu_new_tokens, start_pos, block_tables)
+    return b
 
 
 def decode_batch(q: torch.Tensor, out: torch.Tensor, block_tables: torch.Tensor,
@@ -404,9 +520,11 @@ def decode_batch(q: torch.Tensor, out: torch.Tensor, block_tables: torch.Tensor,
     """The decode part of pkv_mixed_step (arguments as for pkv_paged_attn_decode)."""
     _decode_args(None, q, out, lse, block_tables, context_lens)
     wp, wb = _ws(workspace)
-    return DecodeBatchStruct(_ptr(q), _code_of(q), _ptr(out), _code_of(out), _ptr(lse),
-                             _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
-                             q.shape[0], q.shape[1], max_context_len, split_tokens, wp, wb)
+    b = DecodeBatchStruct(_ptr(q), _code_of(q), _ptr(out), _code_of(out), _ptr(lse),
+                          _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
+                          q.shape[0], q.shape[1], max_context_len, split_tokens, wp, wb)
+    b._tensors = (q, out, lse, block_tables, context_lens, workspace)
+    return b
 
 
 def prefill_batch(q: torch.Tensor, out: torch.Tensor, cu_q_lens: torch.Tensor,
@@ -423,10 +541,12 @@ def prefill_batch(q: torch.Tensor, out: torch.Tensor, cu_q_lens: torch.Tensor,
     R = ctx_before.shape[0]
     _need(cu_q_lens.shape[0] == R + 1 and block_tables.shape[0] == R, "request counts differ")
     wp, wb = _ws(workspace)
-    return PrefillBatchStruct(_ptr(q), _code_of(q), _ptr(out), _code_of(out), _ptr(lse),
-                              _ptr(cu_q_lens), _ptr(ctx_before), _ptr(block_tables),
-                              block_tables.shape[1], R, q.shape[0], q.shape[1], max_chunk_len,
-                              max_total_len, split_tokens, wp, wb)
+    b = PrefillBatchStruct(_ptr(q), _code_of(q), _ptr(out), _code_of(out), _ptr(lse),
+                           _ptr(cu_q_lens), _ptr(ctx_before), _ptr(block_tables),
+                           block_tables.shape[1], R, q.shape[0], q.shape[1], max_chunk_len,
+                           max_total_len, split_tokens, wp, wb)
+    b._tensors = (q, out, lse, cu_q_lens, ctx_before, block_tables, workspace)
+    return b
 
 
 def pkv_mixed_step(cache: PagedCache, append: Optional[AppendBatchStruct],

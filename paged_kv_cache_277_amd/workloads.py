@@ -457,3 +457,16 @@ def prefill_flops(spec: Spec, ctx_before: np.ndarray, cu: np.ndarray) -> int:
         C = int(cu[r + 1] - cu[r])
         pairs += C * P + C * (C + 1) // 2
     return 4 * spec.num_q_heads * spec.head_dim * pairs
+
+
+def request_tensors(seed: int, req_id: int, length: int, num_q_heads: int, num_kv_heads: int,
+                    head_dim: int):
+    """Seeded per-request token data for scheduler-driven runs: q [length][Hq][D]
+    and k, v [length][Hkv][D] as bf16 bits, standard normal, drawn from
+    SeedSequence((seed, req_id)) so a request recomputed after eviction sees
+    the same tokens again."""
+    rng = np.random.default_rng(np.random.SeedSequence((seed, req_id)))
+    q = rng.standard_normal((length, num_q_heads, head_dim), dtype=np.float32)
+    k = rng.standard_normal((length, num_kv_heads, head_dim), dtype=np.float32)
+    v = rng.standard_normal((length, num_kv_heads, head_dim), dtype=np.float32)
+    return bf16_bits_rne(q), bf16_bits_rne(k), bf16_bits_rne(v)
