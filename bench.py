@@ -132,6 +132,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--split-tokens", type=int, default=0)
+    ap.add_argument("--kv-format", choices=("fp8", "int8"), default=None,
+                    help="run the workload with this 8-bit KV format instead (a variant, "
+                         "not one of the five workloads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--launch", choices=("mixed_step", "calls", "graph", "graph_mixed_step"),
@@ -157,7 +160,8 @@ def main() -> int:
     torch.cuda.set_device(0)
     if args.copy_calibration:
         return copy_calibration(args)
-    spec = wk.CONFIGS[args.workload]
+    spec = (wk.variant(f"{args.workload}-{args.kv_format}") if args.kv_format
+            else wk.CONFIGS[args.workload])
     t0 = time.perf_counter()
     wl = wk.make_workload(spec)
     print(f"[bench] workload {spec.name}: generated in {time.perf_counter() - t0:.1f} s",
@@ -236,7 +240,8 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "bf16 q / fp8 e4m3 kv"}[spec.kv_dtype],
+        "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "bf16 q / fp8 e4m3 kv",
+                  "int8": "bf16 q / int8 kv"}[spec.kv_dtype],
         "data": "synthetic (seeded N(0,1) K/V/Q, seeded page permutation)",
         "config": {"workload": spec.name, "num_seqs": spec.num_seqs,
                    "num_q_heads": spec.num_q_heads, "num_kv_heads": spec.num_kv_heads,

@@ -68,13 +68,19 @@ typedef enum pkv_status {
 typedef enum pkv_dtype {
   PKV_F32 = 0,
   PKV_BF16 = 1,
-  PKV_FP8_E4M3FN = 2           /* OCP e4m3fn: bias 7, max 448, no inf, NaN = 0x7F/0xFF */
+  PKV_FP8_E4M3FN = 2,          /* OCP e4m3fn: bias 7, max 448, no inf, NaN = 0x7F/0xFF */
+  PKV_INT8 = 3                 /* symmetric int8 code c in [-127, 127] standing for c * scale
+                                  ("TensorRT-LLM框架解析与高性能推理优化实践" §7.2; the KV-cache
+                                  quantization plugin of "4. TensorRT-LLM架构与核心组件…" §4.3) */
 } pkv_dtype;
 
-/* One layer's paged cache.  Supported: kv_dtype F32, BF16 or FP8_E4M3FN;
+/* One layer's paged cache.  Supported: kv_dtype F32, BF16, FP8_E4M3FN or INT8;
  * head_dim 64 or 128; page_size 16, 32 or 64; num_kv_heads >= 1.
  * k_scale / v_scale: device float[num_kv_heads], required iff kv_dtype is
- * FP8_E4M3FN (stored value = x / scale, dequantised value = code * scale). */
+ * FP8_E4M3FN or INT8 (stored code = encode(x / scale), dequantised value =
+ * code * scale; the division in float32; fp8 rounds to nearest even and
+ * saturates at +-448, int8 rounds half to even and saturates at +-127, NaN
+ * encodes as 0). */
 typedef struct pkv_cache_desc {
   void* k_pool;
   void* v_pool;
@@ -137,7 +143,10 @@ int32_t pkv_page_refcount(const void* alloc, int32_t id);
  *                in_dtype must equal the cache dtype for F32/BF16 caches (a copy);
  *                an FP8 cache takes F32 input and stores
  *                e4m3fn(x / scale[head]): IEEE float32 division, round to
- *                nearest even, saturating to +-448; NaN stays NaN.
+ *                nearest even, saturating to +-448; NaN stays NaN.  An INT8
+ *                cache takes F32 input and stores the integer nearest to
+ *                x / scale[head] (float32 division, ties to even),
+ *                saturated to [-127, 127]; NaN stores 0.
  * cu_new_tokens: device int32[num_rows+1], cu[0] = 0, non-decreasing,
  *                cu[num_rows] = num_new_tokens.
  * start_pos    : device int32[num_rows]; row r's token i goes to logical
@@ -164,7 +173,9 @@ pkv_status pkv_kv_cache_append(const pkv_cache_desc* cache,
  * written directly.
  *
  * Supported (q_dtype, kv_dtype, out_dtype): (F32, F32, F32), (BF16, BF16, BF16),
- * (BF16, FP8_E4M3FN, BF16).  num_q_heads must be a multiple of num_kv_heads
+ * (BF16, FP8_E4M3FN, BF16), (BF16, INT8, BF16).  8-bit codes are widened
+ * exactly to bf16 in the kernel; the per-head scales multiply the scores and
+ * the output.  num_q_heads must be a multiple of num_kv_heads
  * with group size G = num_q_heads / num_kv_heads <= 16.
  *
  * q            : device [num_seqs][num_q_heads][head_dim]

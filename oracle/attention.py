@@ -33,9 +33,11 @@ What the method computes (pages by title and section):
 * Append: each new token's K/V row for every KV head is written to
   ``pool[bt[start + i // P]][j][(start + i) % P]``.  fp32/bf16 caches copy;
   an fp8 cache stores ``e4m3fn(float32(x) / float32(scale[j]))`` with
-  round-to-nearest-even and saturation (§7.2: one scale per head).
+  round-to-nearest-even and saturation (§7.2: one scale per head); an int8
+  cache stores the symmetric code of the same quotient (formats.py).
 
-Storage: "f32" float32 arrays, "bf16" uint16 bit patterns, "fp8" uint8 codes.
+Storage: "f32" float32 arrays, "bf16" uint16 bit patterns, "fp8" uint8 codes,
+"int8" int8 codes.
 """
 from __future__ import annotations
 
@@ -43,21 +45,22 @@ from typing import Optional, Tuple
 
 import numpy as np
 
-from .formats import bf16_to_f64, e4m3fn_to_f64, f32_to_e4m3fn
+from .formats import bf16_to_f64, e4m3fn_to_f64, f32_to_e4m3fn, f32_to_int8_sym, int8_to_f64
 
 
 # ----------------------------------------------------------- storage -------
 def storage_to_f64(raw: np.ndarray, dtype: str, scale: Optional[np.ndarray] = None,
                    head_axis: int = -2) -> np.ndarray:
-    """Decode stored elements to float64; fp8 is multiplied by its head's scale.
+    """Decode stored elements to float64; fp8 and int8 codes are multiplied by
+    their head's scale.
 
-    ``head_axis`` names the KV-head axis of ``raw`` (used only for fp8)."""
+    ``head_axis`` names the KV-head axis of ``raw`` (used only for codes)."""
     if dtype == "f32":
         return np.asarray(raw, dtype=np.float32).astype(np.float64)
     if dtype == "bf16":
         return bf16_to_f64(raw)
-    if dtype == "fp8":
-        x = e4m3fn_to_f64(raw)
+    if dtype in ("fp8", "int8"):
+        x = e4m3fn_to_f64(raw) if dtype == "fp8" else int8_to_f64(raw)
         assert scale is not None
         shape = [1] * x.ndim
         shape[head_axis] = -1
@@ -219,19 +222,21 @@ def kv_cache_append(k_pool: np.ndarray, v_pool: np.ndarray, kv_dtype: str,
     Row r's new token i lands at position start_pos[r] + i of that row:
     page ``block_tables[r][pos // P]``, slot ``pos % P``, for every KV head.
     Copies for fp32/bf16 caches (input dtype must equal the cache dtype); an
-    fp8 cache takes float32 input and stores e4m3fn(x / scale[head]), the
-    division done in float32.  ``rows`` restricts the work to some rows."""
+    fp8 cache takes float32 input and stores e4m3fn(x / scale[head]), an int8
+    cache the symmetric code of x / scale[head], the division done in float32.
+    ``rows`` restricts the work to some rows."""
     P = k_pool.shape[2]
     if rows is None:
         rows = range(start_pos.shape[0])
     for r in rows:
         t0, t1 = int(cu_new[r]), int(cu_new[r + 1])
-        if kv_dtype == "fp8":
+        if kv_dtype in ("fp8", "int8"):
             assert in_dtype == "f32"
+            enc = f32_to_e4m3fn if kv_dtype == "fp8" else f32_to_int8_sym
             ks = np.asarray(k_scale, dtype=np.float32)[None, :, None]
             vs = np.asarray(v_scale, dtype=np.float32)[None, :, None]
-            kq = f32_to_e4m3fn(np.asarray(k_new[t0:t1], dtype=np.float32) / ks)
-            vq = f32_to_e4m3fn(np.asarray(v_new[t0:t1], dtype=np.float32) / vs)
+            kq = enc(np.asarray(k_new[t0:t1], dtype=np.float32) / ks)
+            vq = enc(np.asarray(v_new[t0:t1], dtype=np.float32) / vs)
         else:
             assert in_dtype == kv_dtype
             kq, vq = k_new[t0:t1], v_new[t0:t1]

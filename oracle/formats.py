@@ -76,3 +76,25 @@ def f32_to_e4m3fn(x: np.ndarray) -> np.ndarray:
     code = np.where(nan, 0x7F, code)
     code = code | np.where(neg, 0x80, 0)
     return code.astype(np.uint8)
+
+
+# ------------------------------------------------------------------ int8 ----
+# Symmetric INT8 KV codes with one scale per KV head
+# ("TensorRT-LLM框架解析与高性能推理优化实践" §7.2: a scale per attention head, from
+# the data's statistics; "4. TensorRT-LLM架构与核心组件…" §4.3: the KV-cache
+# quantization plugin stores INT8 or FP8).  Reading: the code of a value x is
+# the float32 quotient x / scale rounded to the nearest integer, ties to even,
+# saturated to [-127, 127] (symmetric: -128 is never produced); NaN encodes
+# as 0.  A code c stands for c * scale.
+INT8_MAX = 127
+
+
+def f32_to_int8_sym(q: np.ndarray) -> np.ndarray:
+    """Code of float32 quotients q = x / scale (already divided)."""
+    q = np.asarray(q, dtype=np.float32).astype(np.float64)     # exact widening
+    r = np.clip(np.rint(q), -INT8_MAX, INT8_MAX)                # rint: ties to even
+    return np.where(np.isnan(q), 0.0, r).astype(np.int8)
+
+
+def int8_to_f64(codes: np.ndarray) -> np.ndarray:
+    return np.asarray(codes, dtype=np.int8).astype(np.float64)

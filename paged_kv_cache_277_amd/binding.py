@@ -24,10 +24,10 @@ LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
 
 PKV_OK, PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_OUT_OF_PAGES, \
     PKV_ERR_BAD_BLOCK_TABLE, PKV_ERR_HIP = range(6)
-PKV_F32, PKV_BF16, PKV_FP8_E4M3FN = 0, 1, 2
+PKV_F32, PKV_BF16, PKV_FP8_E4M3FN, PKV_INT8 = 0, 1, 2, 3
 _STATUS_NAMES = {0: "PKV_OK", 1: "PKV_ERR_INVALID_ARG", 2: "PKV_ERR_UNSUPPORTED",
                  3: "PKV_ERR_OUT_OF_PAGES", 4: "PKV_ERR_BAD_BLOCK_TABLE", 5: "PKV_ERR_HIP"}
-DTYPE_CODES = {"f32": PKV_F32, "bf16": PKV_BF16, "fp8": PKV_FP8_E4M3FN}
+DTYPE_CODES = {"f32": PKV_F32, "bf16": PKV_BF16, "fp8": PKV_FP8_E4M3FN, "int8": PKV_INT8}
 
 
 class PkvError(RuntimeError):
@@ -185,6 +185,8 @@ def _code_of(t: torch.Tensor) -> int:
         return PKV_BF16
     if t.dtype in (torch.uint8, torch.float8_e4m3fn):
         return PKV_FP8_E4M3FN
+    if t.dtype == torch.int8:
+        return PKV_INT8
     raise ValueError(f"unsupported tensor dtype {t.dtype}")
 
 

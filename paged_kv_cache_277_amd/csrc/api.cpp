@@ -43,23 +43,25 @@ pkv_status check_cache(const pkv_cache_desc* c) {
   if (c->num_pages <= 0 || c->num_kv_heads <= 0)
     return fail(PKV_ERR_INVALID_ARG, "num_pages (%d) and num_kv_heads (%d) must be positive",
                 c->num_pages, c->num_kv_heads);
-  if (c->kv_dtype < PKV_F32 || c->kv_dtype > PKV_FP8_E4M3FN)
+  if (c->kv_dtype < PKV_F32 || c->kv_dtype > PKV_INT8)
     return fail(PKV_ERR_INVALID_ARG, "kv_dtype %d is not a pkv_dtype", c->kv_dtype);
   if (c->head_dim != 64 && c->head_dim != 128)
     return fail(PKV_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", c->head_dim);
   if (c->page_size != 16 && c->page_size != 32 && c->page_size != 64)
     return fail(PKV_ERR_UNSUPPORTED, "page_size %d (supported: 16, 32, 64)", c->page_size);
-  if (c->kv_dtype == PKV_FP8_E4M3FN && (!c->k_scale || !c->v_scale))
-    return fail(PKV_ERR_INVALID_ARG, "fp8 cache needs k_scale and v_scale");
-  if (c->kv_dtype != PKV_FP8_E4M3FN && (c->k_scale || c->v_scale))
-    return fail(PKV_ERR_INVALID_ARG, "k_scale/v_scale are only for an fp8 cache");
+  const bool coded = c->kv_dtype == PKV_FP8_E4M3FN || c->kv_dtype == PKV_INT8;
+  if (coded && (!c->k_scale || !c->v_scale))
+    return fail(PKV_ERR_INVALID_ARG, "an fp8 or int8 cache needs k_scale and v_scale");
+  if (!coded && (c->k_scale || c->v_scale))
+    return fail(PKV_ERR_INVALID_ARG, "k_scale/v_scale are only for an fp8 or int8 cache");
   return PKV_OK;
 }
 
 pkv_status check_qo_dtypes(const pkv_cache_desc* c, int32_t q_dtype, int32_t out_dtype) {
   const bool ok = (c->kv_dtype == PKV_F32 && q_dtype == PKV_F32 && out_dtype == PKV_F32) ||
                   (c->kv_dtype == PKV_BF16 && q_dtype == PKV_BF16 && out_dtype == PKV_BF16) ||
-                  (c->kv_dtype == PKV_FP8_E4M3FN && q_dtype == PKV_BF16 && out_dtype == PKV_BF16);
+                  ((c->kv_dtype == PKV_FP8_E4M3FN || c->kv_dtype == PKV_INT8) &&
+                   q_dtype == PKV_BF16 && out_dtype == PKV_BF16);
   if (!ok)
     return fail(PKV_ERR_UNSUPPORTED, "dtype combination q=%d kv=%d out=%d not supported", q_dtype,
                 c->kv_dtype, out_dtype);
@@ -112,7 +114,7 @@ int32_t default_split(const pkv_cache_desc* c, int32_t num_seqs, int32_t num_q_h
     // 16-bit or 1024 of fp8 at head_dim 128); shorter ranges when the batch
     // would give fewer than ~8 items per CU, never below 256 tokens (the merge
     // would cost more than the parallelism gains).
-    split = c->kv_dtype == PKV_FP8_E4M3FN ? 1024 : 512;
+    split = (c->kv_dtype == PKV_FP8_E4M3FN || c->kv_dtype == PKV_INT8) ? 1024 : 512;
     if (c->head_dim == 64) split *= 2;
     const int floor_split = 256;
     while (split / 2 >= floor_split && pairs * ceil_div(std::max(1, max_len), split) < 8 * kNumCUs)
@@ -288,7 +290,8 @@ pkv_status prepare_append(const pkv_cache_desc* cache, const void* k_new, const 
                           pkv::AppendArgs* a) {
   pkv_status st;
   if ((st = check_cache(cache)) != PKV_OK) return st;
-  const int32_t want_in = cache->kv_dtype == PKV_FP8_E4M3FN ? PKV_F32 : cache->kv_dtype;
+  const int32_t want_in =
+      (cache->kv_dtype == PKV_FP8_E4M3FN || cache->kv_dtype == PKV_INT8) ? PKV_F32 : cache->kv_dtype;
   if (in_dtype != want_in)
     return fail(PKV_ERR_UNSUPPORTED, "append into kv_dtype %d takes in_dtype %d, got %d",
                 cache->kv_dtype, want_in, in_dtype);

@@ -4,7 +4,8 @@
 // position maps to a physical page through the request's block table
 // ("TensorRT-LLM框架解析与高性能推理优化实践" §4.2; in-flight batching places each
 // request's KV as it grows, "TensorRT-LLM内核融合与动态批处理", In-flight Batching).
-// An fp8 cache stores x / scale[head] rounded to e4m3fn (first page, §7.2).
+// An fp8 cache stores x / scale[head] rounded to e4m3fn, an int8 cache its
+// symmetric int8 code (first page, §7.2: one scale per head).
 //
 // Launch: one workgroup per new token; its threads cover the token's
 // Hkv x head_dim row in 16-byte output pieces, so every page row is written
@@ -34,8 +35,8 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     const int j = c / pieces, pc = c % pieces;
     const size_t dst = ((((size_t)page * Hkv + j) * P + slot) * D + (size_t)pc * EPL) * KVB;
     const size_t src_e = ((size_t)t * Hkv + j) * D + (size_t)pc * EPL;   // input element
-    if constexpr (KVT == KV_FP8) {
-      // F32 input: 16 floats -> 16 codes.
+    if constexpr (KvCoded<KVT>::value) {
+      // F32 input: 16 floats -> 16 codes (fp8 or int8).
       const float ks = a.c.k_scale[j], vs = a.c.v_scale[j];
       const u32x4* ksrc = reinterpret_cast<const u32x4*>(static_cast<const float*>(a.k_new) + src_e);
       const u32x4* vsrc = reinterpret_cast<const u32x4*>(static_cast<const float*>(a.v_new) + src_e);
@@ -46,8 +47,8 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
         uint32_t kw = 0, vw = 0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          kw |= f32_to_e4m3fn(__uint_as_float(kx[e]) / ks) << (8 * e);
-          vw |= f32_to_e4m3fn(__uint_as_float(vx[e]) / vs) << (8 * e);
+          kw |= f32_to_code<KVT>(__uint_as_float(kx[e]) / ks) << (8 * e);
+          vw |= f32_to_code<KVT>(__uint_as_float(vx[e]) / vs) << (8 * e);
         }
         ko[q4] = kw;
         vo[q4] = vw;
@@ -87,7 +88,8 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
   switch (a.c.kv_dtype) {
     case KV_F32: hipLaunchKernelGGL(append_kernel<KV_F32>, grid, block, 0, s, a); break;
     case KV_BF16: hipLaunchKernelGGL(append_kernel<KV_BF16>, grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL(append_kernel<KV_FP8>, grid, block, 0, s, a); break;
+    case KV_FP8: hipLaunchKernelGGL(append_kernel<KV_FP8>, grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL(append_kernel<KV_INT8>, grid, block, 0, s, a); break;
   }
   return hipGetLastError();
 }

@@ -57,7 +57,7 @@ __device__ __forceinline__ void piece_to_f32(const u32x4& x, float* o) {
     for (int i = 0; i < 4; ++i) { o[2 * i] = bf16_lo(x[i]); o[2 * i + 1] = bf16_hi(x[i]); }
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fp8x4_to_f32(x[i], o + 4 * i);
+    for (int i = 0; i < 4; ++i) code4_to_f32<KVT>(x[i], o + 4 * i);
   }
 }
 
@@ -154,7 +154,7 @@ __global__ __launch_bounds__(256) void decode_partial_vec(AttnArgs a) {
   const int rg = lane / R, col = lane % R;
 
   float kscale = 1.0f, vscale = 1.0f;
-  if constexpr (KVT == KV_FP8) { kscale = a.c.k_scale[j]; vscale = a.c.v_scale[j]; }
+  if constexpr (KvCoded<KVT>::value) { kscale = a.c.k_scale[j]; vscale = a.c.v_scale[j]; }
   const float qmul = a.sm_scale * kLog2e * kscale;
 
   float qf[GMAX][EPL];
@@ -423,7 +423,8 @@ hipError_t launch_vec_any(const AttnArgs& a, dim3 grid, hipStream_t s) {
   switch (a.c.kv_dtype) {
     case KV_F32: return launch_vec<KV_F32>(a, grid, s);
     case KV_BF16: return launch_vec<KV_BF16>(a, grid, s);
-    default: return launch_vec<KV_FP8>(a, grid, s);
+    case KV_FP8: return launch_vec<KV_FP8>(a, grid, s);
+    default: return launch_vec<KV_INT8>(a, grid, s);
   }
 }
 

@@ -55,13 +55,6 @@ __device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, const f3
                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-// 16 fp8 codes -> 16 bf16 (two u32x4).
-__device__ __forceinline__ void fp8x16_to_bf16(const u32x4& x, u32x4& lo, u32x4& hi) {
-  lo[0] = fp8x2_to_bf16x2<false>(x[0]); lo[1] = fp8x2_to_bf16x2<true>(x[0]);
-  lo[2] = fp8x2_to_bf16x2<false>(x[1]); lo[3] = fp8x2_to_bf16x2<true>(x[1]);
-  hi[0] = fp8x2_to_bf16x2<false>(x[2]); hi[1] = fp8x2_to_bf16x2<true>(x[2]);
-  hi[2] = fp8x2_to_bf16x2<false>(x[3]); hi[3] = fp8x2_to_bf16x2<true>(x[3]);
-}
 
 
 // Per-lane register image of one 32-token tile, K and V alike: lane l holds
@@ -89,10 +82,10 @@ __device__ __forceinline__ void tile_pages(const int32_t* pages,
 
 // First of the 8 consecutive d values that MFMA step kk takes for lane group g:
 // K load i of a lane holds 16-byte piece 4i + g of its token row, i.e. 8 bf16
-// (step kk = i) or 16 fp8 codes (steps 2i and 2i + 1).
+// (step kk = i) or 16 8-bit codes (steps 2i and 2i + 1).
 template <int KVT>
 __device__ __forceinline__ int k_elem_offset(int kk, int g) {
-  if constexpr (KVT == KV_FP8) return 64 * (kk >> 1) + 16 * g + 8 * (kk & 1);
+  if constexpr (KvCoded<KVT>::value) return 64 * (kk >> 1) + 16 * g + 8 * (kk & 1);
   else return 32 * kk + 8 * g;
 }
 
@@ -159,7 +152,7 @@ __global__ __launch_bounds__(256, 2) void decode_partial_mfma(AttnArgs a) {
   const int pshift = a.page_shift;
 
   float kscale = 1.0f, vscale = 1.0f;
-  if constexpr (KVT == KV_FP8) { kscale = a.c.k_scale[j]; vscale = a.c.v_scale[j]; }
+  if constexpr (KvCoded<KVT>::value) { kscale = a.c.k_scale[j]; vscale = a.c.v_scale[j]; }
   const float smul = a.sm_scale * kLog2e * kscale;
 
   // Q^T as B operand: lane (g, h) holds Q[j*G + h][d] for the d's that MFMA
@@ -234,13 +227,13 @@ __global__ __launch_bounds__(256, 2) void decode_partial_mfma(AttnArgs a) {
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         u32x4 ka;
-        if constexpr (KVT == KV_FP8) {
+        if constexpr (KvCoded<KVT>::value) {
           const u32x4 src = *reinterpret_cast<const u32x4*>(krow + 64 * (kk >> 1));
           const int o2 = (kk & 1) * 2;
-          ka[0] = fp8x2_to_bf16x2<false>(src[o2]);
-          ka[1] = fp8x2_to_bf16x2<true>(src[o2]);
-          ka[2] = fp8x2_to_bf16x2<false>(src[o2 + 1]);
-          ka[3] = fp8x2_to_bf16x2<true>(src[o2 + 1]);
+          ka[0] = code2_to_bf16x2<KVT, false>(src[o2]);
+          ka[1] = code2_to_bf16x2<KVT, true>(src[o2]);
+          ka[2] = code2_to_bf16x2<KVT, false>(src[o2 + 1]);
+          ka[3] = code2_to_bf16x2<KVT, true>(src[o2 + 1]);
         } else {
           ka = *reinterpret_cast<const u32x4*>(krow + 64 * kk);
         }
@@ -293,9 +286,9 @@ __global__ __launch_bounds__(256, 2) void decode_partial_mfma(AttnArgs a) {
         const int tok = 16 * blk + rr;
         u32x4 x = cur.v[blk * LPB + i];
         if (!full && t0 + tok >= t_end) x = u32x4{0, 0, 0, 0};
-        if constexpr (KVT == KV_FP8) {
+        if constexpr (KvCoded<KVT>::value) {
           u32x4 lo, hi;
-          fp8x16_to_bf16(x, lo, hi);
+          code16_to_bf16<KVT>(x, lo, hi);
           uint8_t* dst = lds + tok * LDS_ROW + (lane % R) * 32;
           *reinterpret_cast<u32x4*>(dst) = lo;
           *reinterpret_cast<u32x4*>(dst + 16) = hi;
@@ -397,9 +390,12 @@ hipError_t launch_decode_partial_mfma(const AttnArgs& a, hipStream_t s) {
   if (a.c.kv_dtype == KV_BF16) {
     if (a.c.head_dim == 128) hipLaunchKernelGGL((decode_partial_mfma<KV_BF16, 128>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((decode_partial_mfma<KV_BF16, 64>), grid, block, 0, s, a);
-  } else {
+  } else if (a.c.kv_dtype == KV_FP8) {
     if (a.c.head_dim == 128) hipLaunchKernelGGL((decode_partial_mfma<KV_FP8, 128>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((decode_partial_mfma<KV_FP8, 64>), grid, block, 0, s, a);
+  } else {
+    if (a.c.head_dim == 128) hipLaunchKernelGGL((decode_partial_mfma<KV_INT8, 128>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((decode_partial_mfma<KV_INT8, 64>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }

@@ -18,12 +18,17 @@
 
 namespace pkv {
 
-enum KvType : int { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };
+enum KvType : int { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2, KV_INT8 = 3 };
 
 template <int KVT> struct KvBytes;
 template <> struct KvBytes<KV_F32> { static constexpr int value = 4; };
 template <> struct KvBytes<KV_BF16> { static constexpr int value = 2; };
 template <> struct KvBytes<KV_FP8> { static constexpr int value = 1; };
+template <> struct KvBytes<KV_INT8> { static constexpr int value = 1; };
+
+// 8-bit codes with one scale per KV head (fp8 e4m3fn or symmetric int8):
+// stored code = encode(x / scale), value = code * scale.
+template <int KVT> struct KvCoded { static constexpr bool value = KVT == KV_FP8 || KVT == KV_INT8; };
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -96,6 +101,36 @@ __device__ __forceinline__ uint32_t f32_to_e4m3fn(float y) {
   return sign | ((e << 3) + keep + up);
 }
 
+// Symmetric int8 code of a float32 quotient q = x / scale: the nearest
+// integer, ties to even (v_rndne), saturated to [-127, 127]; NaN -> 0.
+__device__ __forceinline__ uint32_t f32_to_int8_sym(float q) {
+  if (q != q) return 0u;
+  const float r = fminf(fmaxf(__builtin_rintf(q), -127.0f), 127.0f);
+  return uint32_t(int32_t(r)) & 0xFFu;
+}
+
+template <int KVT>
+__device__ __forceinline__ uint32_t f32_to_code(float q) {
+  if constexpr (KVT == KV_FP8) return f32_to_e4m3fn(q);
+  else return f32_to_int8_sym(q);
+}
+
+// Four int8 codes (one dword, byte 0 first) -> four floats (exact).
+__device__ __forceinline__ void int8x4_to_f32(uint32_t w, float* o) {
+  o[0] = float(int8_t(w));
+  o[1] = float(int8_t(w >> 8));
+  o[2] = float(int8_t(w >> 16));
+  o[3] = float(int8_t(w >> 24));
+}
+
+// Two int8 codes (bytes 2*HI, 2*HI+1 of w) -> two bf16 in a dword (exact:
+// integers of magnitude <= 128 are bf16 values).
+template <bool HI>
+__device__ __forceinline__ uint32_t int8x2_to_bf16x2(uint32_t w) {
+  const uint32_t x = HI ? (w >> 16) : w;
+  return pack_bf16x2(float(int8_t(x)), float(int8_t(x >> 8)));
+}
+
 // 16 bytes from global memory.
 __device__ __forceinline__ u32x4 ld16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
@@ -155,6 +190,28 @@ __device__ __forceinline__ int owner_row(const int32_t* cu, int n, int t) {
     if (cu[mid] <= t) lo = mid; else hi = mid;
   }
   return lo;
+}
+
+// Generic 8-bit code converters (fp8 e4m3fn or int8), exact.
+template <int KVT>
+__device__ __forceinline__ void code4_to_f32(uint32_t w, float* o) {
+  if constexpr (KVT == KV_FP8) fp8x4_to_f32(w, o);
+  else int8x4_to_f32(w, o);
+}
+
+template <int KVT, bool HI>
+__device__ __forceinline__ uint32_t code2_to_bf16x2(uint32_t w) {
+  if constexpr (KVT == KV_FP8) return fp8x2_to_bf16x2<HI>(w);
+  else return int8x2_to_bf16x2<HI>(w);
+}
+
+// 16 codes -> 16 bf16 (lo: codes 0..7, hi: codes 8..15).
+template <int KVT>
+__device__ __forceinline__ void code16_to_bf16(const u32x4& x, u32x4& lo, u32x4& hi) {
+  lo[0] = code2_to_bf16x2<KVT, false>(x[0]); lo[1] = code2_to_bf16x2<KVT, true>(x[0]);
+  lo[2] = code2_to_bf16x2<KVT, false>(x[1]); lo[3] = code2_to_bf16x2<KVT, true>(x[1]);
+  hi[0] = code2_to_bf16x2<KVT, false>(x[2]); hi[1] = code2_to_bf16x2<KVT, true>(x[2]);
+  hi[2] = code2_to_bf16x2<KVT, false>(x[3]); hi[3] = code2_to_bf16x2<KVT, true>(x[3]);
 }
 
 }  // namespace pkv

@@ -119,16 +119,10 @@ __device__ __forceinline__ void pf_store(PfRegs<KVT, D> r, uint8_t* kl, uint8_t*
     const int piece = threadIdx.x + 256 * i;
     const int tok = piece / PR, pc = piece % PR;
     if (piece >= S::PIECES) continue;
-    if constexpr (KVT == KV_FP8) {
+    if constexpr (KvCoded<KVT>::value) {
       u32x4 klo, khi, vlo, vhi;
-      klo[0] = fp8x2_to_bf16x2<false>(r.k[i][0]); klo[1] = fp8x2_to_bf16x2<true>(r.k[i][0]);
-      klo[2] = fp8x2_to_bf16x2<false>(r.k[i][1]); klo[3] = fp8x2_to_bf16x2<true>(r.k[i][1]);
-      khi[0] = fp8x2_to_bf16x2<false>(r.k[i][2]); khi[1] = fp8x2_to_bf16x2<true>(r.k[i][2]);
-      khi[2] = fp8x2_to_bf16x2<false>(r.k[i][3]); khi[3] = fp8x2_to_bf16x2<true>(r.k[i][3]);
-      vlo[0] = fp8x2_to_bf16x2<false>(r.v[i][0]); vlo[1] = fp8x2_to_bf16x2<true>(r.v[i][0]);
-      vlo[2] = fp8x2_to_bf16x2<false>(r.v[i][1]); vlo[3] = fp8x2_to_bf16x2<true>(r.v[i][1]);
-      vhi[0] = fp8x2_to_bf16x2<false>(r.v[i][2]); vhi[1] = fp8x2_to_bf16x2<true>(r.v[i][2]);
-      vhi[2] = fp8x2_to_bf16x2<false>(r.v[i][3]); vhi[3] = fp8x2_to_bf16x2<true>(r.v[i][3]);
+      code16_to_bf16<KVT>(r.k[i], klo, khi);
+      code16_to_bf16<KVT>(r.v[i], vlo, vhi);
       *reinterpret_cast<u32x4*>(kl + tok * S::K_LDS + pc * 32) = klo;
       *reinterpret_cast<u32x4*>(kl + tok * S::K_LDS + pc * 32 + 16) = khi;
       *reinterpret_cast<u32x4*>(vl + tok * S::V_LDS + pc * 32) = vlo;
@@ -189,7 +183,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma(AttnArgs a, int nqb, int 
   const int wave_min_lim = Pr + wrow0 / G;       // smallest key limit in the wave
 
   float kscale = 1.0f, vscale = 1.0f;
-  if constexpr (KVT == KV_FP8) { kscale = a.c.k_scale[j]; vscale = a.c.v_scale[j]; }
+  if constexpr (KvCoded<KVT>::value) { kscale = a.c.k_scale[j]; vscale = a.c.v_scale[j]; }
   const float smul = a.sm_scale * kLog2e * kscale;
 
   // Per N-tile nt: this lane's row (column n of S^T / O^T) and its Q^T
@@ -410,9 +404,12 @@ hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t s) {
   if (a.c.kv_dtype == KV_BF16) {
     if (a.c.head_dim == 128) hipLaunchKernelGGL((prefill_mfma<KV_BF16, 128>), grid, block, 0, s, a, nqb, npg);
     else hipLaunchKernelGGL((prefill_mfma<KV_BF16, 64>), grid, block, 0, s, a, nqb, npg);
-  } else {
+  } else if (a.c.kv_dtype == KV_FP8) {
     if (a.c.head_dim == 128) hipLaunchKernelGGL((prefill_mfma<KV_FP8, 128>), grid, block, 0, s, a, nqb, npg);
     else hipLaunchKernelGGL((prefill_mfma<KV_FP8, 64>), grid, block, 0, s, a, nqb, npg);
+  } else {
+    if (a.c.head_dim == 128) hipLaunchKernelGGL((prefill_mfma<KV_INT8, 128>), grid, block, 0, s, a, nqb, npg);
+    else hipLaunchKernelGGL((prefill_mfma<KV_INT8, 64>), grid, block, 0, s, a, nqb, npg);
   }
   return hipGetLastError();
 }

@@ -18,11 +18,12 @@ import torch
 from . import binding as B
 from .workloads import POISON, Workload
 
-_TORCH_STORAGE = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}
+_TORCH_STORAGE = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8,
+                  "int8": torch.int8}
 
 
 def _dev(x: np.ndarray, dtype: str, device) -> torch.Tensor:
-    """numpy array (float32 / uint16 bf16 bits / uint8 / int32) -> device tensor."""
+    """numpy array (float32 / uint16 bf16 bits / uint8 / int8 / int32) -> device tensor."""
     x = np.ascontiguousarray(x)
     if dtype == "bf16":
         return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(device)
@@ -30,6 +31,8 @@ def _dev(x: np.ndarray, dtype: str, device) -> torch.Tensor:
         return torch.from_numpy(x.astype(np.float32, copy=False)).to(device)
     if dtype == "fp8":
         return torch.from_numpy(x.astype(np.uint8, copy=False)).to(device)
+    if dtype == "int8":
+        return torch.from_numpy(x.astype(np.int8, copy=False)).to(device)
     if dtype == "i32":
         return torch.from_numpy(x.astype(np.int32, copy=False)).to(device)
     raise ValueError(dtype)
@@ -43,6 +46,8 @@ def poisoned_pool(num_pages: int, Hkv: int, P: int, D: int, kv_dtype: str, devic
     if kv_dtype == "bf16":
         return torch.full(shape, int(POISON["bf16"].view(np.int16)), dtype=torch.int16,
                           device=device).view(torch.bfloat16)
+    if kv_dtype == "int8":
+        return torch.full(shape, int(POISON["int8"]), dtype=torch.int8, device=device)
     return torch.full(shape, int(POISON["fp8"]), dtype=torch.uint8, device=device)
 
 
@@ -170,7 +175,7 @@ def upload(wl: Workload, device="cuda", split_tokens: int = 0,
     kp = poisoned_pool(wl.num_pages, s.num_kv_heads, s.page_size, s.head_dim, s.kv_dtype, device)
     vp = poisoned_pool(wl.num_pages, s.num_kv_heads, s.page_size, s.head_dim, s.kv_dtype, device)
     ks = vs = None
-    if s.kv_dtype == "fp8":
+    if s.kv_dtype in ("fp8", "int8"):
         ks = torch.from_numpy(wl.k_scale).to(device)
         vs = torch.from_numpy(wl.v_scale).to(device)
     cache = B.PagedCache(kp, vp, ks, vs)

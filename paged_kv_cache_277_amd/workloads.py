@@ -24,11 +24,14 @@ Recipe (every decision that the shapes leave open is written here):
     ceil(1.25 * pages needed) pages unless the workload fixes the count;
     shared prefix pages are taken once, first;
   * values: standard normal float32; bf16 inputs are the RNE cast of those
-    draws (carried as uint16 bit patterns), fp8 caches take float32 inputs;
-  * fp8 scale per KV head: float32(amax / 448) over every drawn token of that
-    head (the workload's calibration recipe, an input of the method);
-  * every pool byte that no token occupies is a NaN (poison), so a read of an
-    unused slot shows up in the result.
+    draws (carried as uint16 bit patterns), fp8 and int8 caches take float32
+    inputs;
+  * scale per KV head: float32(amax / 448) for fp8, float32(amax / 127) for
+    int8, over every drawn token of that head (the workload's calibration
+    recipe, an input of the method);
+  * every pool byte that no token occupies is a NaN (poison) — for int8,
+    which has none, the code -128 that the symmetric encoding never writes —
+    so a read of an unused slot shows up in the result.
 """
 from __future__ import annotations
 
@@ -43,10 +46,13 @@ import numpy as np
 SEED_BASE = 20261202
 
 # Element sizes of the storage dtypes, in bytes.
-DTYPE_BYTES = {"f32": 4, "bf16": 2, "fp8": 1}
-# NaN bit patterns used to poison unused pool bytes.
-POISON = {"f32": np.uint32(0x7FC00000), "bf16": np.uint16(0x7FC0), "fp8": np.uint8(0x7F)}
-STORAGE_NP = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}
+DTYPE_BYTES = {"f32": 4, "bf16": 2, "fp8": 1, "int8": 1}
+# Bit patterns used to poison unused pool bytes (NaN; int8: the unused code -128).
+POISON = {"f32": np.uint32(0x7FC00000), "bf16": np.uint16(0x7FC0), "fp8": np.uint8(0x7F),
+          "int8": np.int8(-128)}
+STORAGE_NP = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8, "int8": np.int8}
+# Largest code magnitude of the 8-bit KV formats (scale = amax / this).
+CODE_MAX = {"fp8": 448.0, "int8": 127.0}
 
 
 def _threads() -> int:
@@ -82,7 +88,7 @@ class Spec:
     head_dim: int
     page_size: int
     q_dtype: str                   # "f32" | "bf16"
-    kv_dtype: str                  # "f32" | "bf16" | "fp8"
+    kv_dtype: str                  # "f32" | "bf16" | "fp8" | "int8"
     out_dtype: str                 # "f32" | "bf16"
     lens: LenDist
     num_pages: Optional[int] = None
@@ -101,8 +107,8 @@ class Spec:
 
     @property
     def kv_in_dtype(self) -> str:
-        """Dtype of the new K/V handed to the append (fp8 caches quantize f32)."""
-        return "f32" if self.kv_dtype == "fp8" else self.kv_dtype
+        """Dtype of the new K/V handed to the append (8-bit caches quantize f32)."""
+        return "f32" if self.kv_dtype in CODE_MAX else self.kv_dtype
 
 
 # The five workloads: tiny fp32; 13B-shaped MHA bf16; 8B-shaped GQA bf16 with a
@@ -339,15 +345,16 @@ def make_workload(spec: Spec, seed: Optional[int] = None) -> Workload:
     fkv.run()
 
     k_scale = v_scale = None
-    if spec.kv_dtype == "fp8":
+    if spec.kv_dtype in CODE_MAX:
         ka = np.zeros(Hkv, np.float32)
         va = np.zeros(Hkv, np.float32)
         for key in logical_k:
             if logical_k[key].shape[0]:
                 ka = np.maximum(ka, np.abs(logical_k[key]).max(axis=(0, 2)))
                 va = np.maximum(va, np.abs(logical_v[key]).max(axis=(0, 2)))
-        k_scale = (ka / np.float32(448.0)).astype(np.float32)
-        v_scale = (va / np.float32(448.0)).astype(np.float32)
+        cmax = np.float32(CODE_MAX[spec.kv_dtype])
+        k_scale = (ka / cmax).astype(np.float32)
+        v_scale = (va / cmax).astype(np.float32)
 
     def build(rows) -> AppendBatch:
         n = len(rows)
@@ -445,7 +452,7 @@ def decode_bytes(spec: Spec, context_lens: np.ndarray, unique_prefix: bool = Tru
     B = int(L.shape[0])
     qo = B * spec.num_q_heads * spec.head_dim * (DTYPE_BYTES[spec.q_dtype] + DTYPE_BYTES[spec.out_dtype])
     bt = 4 * (B + int((-(-L // spec.page_size)).sum()))
-    sc = 8 * spec.num_kv_heads if spec.kv_dtype == "fp8" else 0
+    sc = 8 * spec.num_kv_heads if spec.kv_dtype in CODE_MAX else 0
     return tok * row + qo + bt + sc
 
 
@@ -470,3 +477,15 @@ def request_tensors(seed: int, req_id: int, length: int, num_q_heads: int, num_k
     k = rng.standard_normal((length, num_kv_heads, head_dim), dtype=np.float32)
     v = rng.standard_normal((length, num_kv_heads, head_dim), dtype=np.float32)
     return bf16_bits_rne(q), bf16_bits_rne(k), bf16_bits_rne(v)
+
+
+def variant(name: str) -> Spec:
+    """A workload of CONFIGS with another KV format: "<id>-int8" or "<id>-fp8"
+    (same shapes, lengths and seed stream; the scales follow the format)."""
+    import dataclasses
+    wid, kv = name.split("-")
+    base = CONFIGS[int(wid)]
+    tag = {"int8": "int8kv", "fp8": "fp8kv"}[kv]
+    stem = base.name.replace("_fp8kv", "").replace("_bf16", "")
+    return dataclasses.replace(base, kv_dtype=kv, name=f"{stem}_{tag}")
+

@@ -124,6 +124,8 @@ def _decode(desc, q_dtype=B.PKV_BF16, out_dtype=B.PKV_BF16, Hq=4, max_len=64, st
     (dict(num_pages=0), B.PKV_ERR_INVALID_ARG),
     (dict(kv_dtype=B.PKV_FP8_E4M3FN), B.PKV_ERR_INVALID_ARG),          # fp8 without scales
     (dict(k_scale=FAKE, v_scale=FAKE), B.PKV_ERR_INVALID_ARG),          # scales on bf16
+    (dict(kv_dtype=B.PKV_INT8), B.PKV_ERR_INVALID_ARG),                  # int8 without scales
+    (dict(kv_dtype=4, k_scale=FAKE, v_scale=FAKE), B.PKV_ERR_INVALID_ARG),  # not a dtype
 ])
 def test_decode_rejects_bad_cache(kw, status):
     assert _decode(_desc(**kw)) == status
@@ -147,6 +149,9 @@ def test_decode_rejects_bad_arguments():
     assert b"workspace" in B.lib().pkv_last_error()
     f8 = _desc(kv_dtype=B.PKV_FP8_E4M3FN, k_scale=FAKE, v_scale=FAKE)
     assert _decode(f8, q_dtype=B.PKV_F32, out_dtype=B.PKV_F32) == B.PKV_ERR_UNSUPPORTED
+    i8 = _desc(kv_dtype=B.PKV_INT8, k_scale=FAKE, v_scale=FAKE)
+    assert _decode(i8, q_dtype=B.PKV_F32, out_dtype=B.PKV_F32) == B.PKV_ERR_UNSUPPORTED
+    assert _decode(i8, out_dtype=B.PKV_F32) == B.PKV_ERR_UNSUPPORTED
 
 
 def test_workspace_and_split_planning():
@@ -170,9 +175,12 @@ def test_append_and_prefill_reject_on_host():
     # bf16 cache takes bf16 input
     assert lib.pkv_kv_cache_append(C.byref(d), FAKE, FAKE, B.PKV_F32, FAKE, FAKE, FAKE, 4, 1, 1,
                                    None) == B.PKV_ERR_UNSUPPORTED
-    # fp8 cache takes f32 input
+    # fp8 and int8 caches take f32 input
     f8 = _desc(kv_dtype=B.PKV_FP8_E4M3FN, k_scale=FAKE, v_scale=FAKE)
     assert lib.pkv_kv_cache_append(C.byref(f8), FAKE, FAKE, B.PKV_BF16, FAKE, FAKE, FAKE, 4, 1, 1,
+                                   None) == B.PKV_ERR_UNSUPPORTED
+    i8 = _desc(kv_dtype=B.PKV_INT8, k_scale=FAKE, v_scale=FAKE)
+    assert lib.pkv_kv_cache_append(C.byref(i8), FAKE, FAKE, B.PKV_INT8, FAKE, FAKE, FAKE, 4, 1, 1,
                                    None) == B.PKV_ERR_UNSUPPORTED
     assert lib.pkv_kv_cache_append(C.byref(d), None, FAKE, B.PKV_BF16, FAKE, FAKE, FAKE, 4, 1, 1,
                                    None) == B.PKV_ERR_INVALID_ARG

@@ -21,8 +21,10 @@ from tests import _support as sup
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"f32": (1e-4, None), "bf16": (2e-2, 2e-3), "fp8": (6e-2, None)}
-LSE_TOL = {"f32": 1e-4, "bf16": 2e-3, "fp8": 2e-3}
+# int8: the codes widen exactly to bf16 and the arithmetic after that is the
+# bf16 path's (scales applied in fp32), so the bf16 bar applies.
+TOL = {"f32": (1e-4, None), "bf16": (2e-2, 2e-3), "fp8": (6e-2, None), "int8": (2e-2, 2e-3)}
+LSE_TOL = {"f32": 1e-4, "bf16": 2e-3, "fp8": 2e-3, "int8": 2e-3}
 
 
 def _kind(spec):
@@ -59,7 +61,7 @@ def spec_of(lens, Hq, Hkv, D, P, kv, **kw):
 def gpu_cache_from(wl, kp, vp):
     s = wl.spec
     ks = vs = None
-    if s.kv_dtype == "fp8":
+    if s.kv_dtype in ("fp8", "int8"):
         ks = torch.from_numpy(wl.k_scale).cuda()
         vs = torch.from_numpy(wl.v_scale).cuda()
     return B.PagedCache(dev._dev(kp, s.kv_dtype, "cuda"), dev._dev(vp, s.kv_dtype, "cuda"), ks, vs)
@@ -100,6 +102,8 @@ APPEND_CASES = [
     ((1, 15, 16, 17, 63, 64, 65), 8, 2, 128, 64, "bf16"),
     ((5, 31, 32, 33, 200), 8, 1, 128, 32, "fp8"),
     ((3, 70, 129), 16, 4, 64, 16, "fp8"),
+    ((5, 31, 32, 33, 200), 8, 1, 128, 32, "int8"),
+    ((3, 70, 129), 16, 4, 64, 16, "int8"),
 ]
 
 
@@ -139,6 +143,30 @@ def test_append_fp8_rounding_edges():
     assert dev.storage_to_numpy(dw.cache.v_pool).tobytes() == vp.tobytes()
 
 
+def test_append_int8_rounding_edges():
+    """Quotients at and around every half-integer tie, saturation, infinities
+    and NaN (which encodes as 0); scale 1 so the quotient is the value."""
+    spec = spec_of((40,), 2, 2, 64, 16, "int8")
+    wl = wk.make_workload(spec, seed=4)
+    ties = (np.arange(-130, 131) + 0.5).astype(np.float32)
+    probe = np.concatenate([ties, np.nextafter(ties, np.float32(1e9)),
+                            np.nextafter(ties, np.float32(-1e9)),
+                            np.array([127.0, 127.49, 127.5, 128.0, 1e30, np.inf, np.nan, 0.0, -0.0,
+                                      1e-30], np.float32)])
+    probe = np.concatenate([probe, -probe]).astype(np.float32)
+    flat = wl.setup.k.reshape(-1)
+    flat[:] = np.resize(probe, flat.shape)
+    wl.setup.v.reshape(-1)[:] = np.resize(probe[::-1], flat.shape)
+    wl.k_scale[:] = 1.0
+    wl.v_scale[:] = 1.0
+    dw = dev.upload(wl)
+    dw.setup()
+    torch.cuda.synchronize()
+    kp, vp = sup.oracle_pools(wl, with_step=False)
+    assert dev.storage_to_numpy(dw.cache.k_pool).tobytes() == kp.tobytes()
+    assert dev.storage_to_numpy(dw.cache.v_pool).tobytes() == vp.tobytes()
+
+
 # ---------------------------------------------------------------- decode ----
 DECODE_CASES = [
     # lens, Hq, Hkv, D, P, kv
@@ -153,6 +181,10 @@ DECODE_CASES = [
     ((1, 31, 200), 4, 2, 128, 32, "fp8"),                 # G 2: fp8 on the vector path
     ((1, 31, 200), 12, 4, 128, 32, "fp8"),                # G 3: smallest matrix-core group
     ((17, 250), 48, 4, 64, 64, "bf16"),                   # G 12, D 64
+    ((1, 64, 65, 1500), 64, 8, 128, 64, "int8"),          # GQA 8, int8 KV (matrix cores)
+    ((5, 100, 333), 8, 1, 64, 16, "int8"),                # G 8, D 64, page 16
+    ((1, 31, 200), 4, 2, 128, 32, "int8"),                # G 2: int8 on the vector path
+    ((7, 33, 64), 4, 4, 64, 16, "int8"),                  # G 1, D 64
 ]
 
 
@@ -241,6 +273,8 @@ PREFILL_CASES = [
     ((9,), 12, 4, 64, 16, "bf16", (3, 40), 33),               # G 3, page 16, ragged tiles
     ((9,), 16, 16, 128, 64, "bf16", (100,), 77),              # G 1 on the matrix cores
     ((9,), 8, 1, 64, 32, "fp8", (31,), 45),                   # G 8, fp8, head_dim 64
+    ((9,), 16, 2, 128, 64, "int8", (64, 1), 70),              # int8 KV
+    ((9,), 8, 1, 64, 32, "int8", (31, 100), 45),              # int8, head_dim 64
 ]
 
 
@@ -301,9 +335,9 @@ def _sample(n, k, seed):
     return np.sort(rng.choice(n, size=min(n, k), replace=False))
 
 
-@pytest.mark.parametrize("cfg,nsample", [(2, 6), (3, 12), (4, 4)])
+@pytest.mark.parametrize("cfg,nsample", [(2, 6), (3, 12), (4, 4), ("4-int8", 4)])
 def test_decode_full_size_sampled(cfg, nsample):
-    spec = wk.CONFIGS[cfg]
+    spec = wk.CONFIGS[cfg] if cfg in wk.CONFIGS else wk.variant(cfg)
     wl = wk.make_workload(spec)
     print(f"[full-size decode] workload {cfg} B={wl.num_seqs} pages={wl.num_pages}", flush=True)
     dw = dev.upload(wl)
@@ -311,7 +345,8 @@ def test_decode_full_size_sampled(cfg, nsample):
     dw.step()
     torch.cuda.synchronize()
     L = wl.context_lens
-    pick = np.unique(np.concatenate([_sample(wl.num_seqs, nsample - 2, cfg),
+    seed = cfg if isinstance(cfg, int) else int(cfg.split("-")[0])
+    pick = np.unique(np.concatenate([_sample(wl.num_seqs, nsample - 2, seed),
                                      [int(np.argmax(L)), int(np.argmin(L))]]))
     owners = [("seq", int(b)) for b in pick]
     kp, vp = sup.oracle_pools(wl, setup_rows=sup.rows_touching(wl.setup, owners),

@@ -32,6 +32,7 @@ SMALL = [
     ((31, 32, 33, 95), 8, 2, 64, 32, "bf16", "bf16"),
     ((5, 64, 65, 130), 8, 1, 16, 64, "bf16", "fp8"),
     ((3, 70), 16, 2, 64, 32, "f32", "f32"),
+    ((5, 64, 65, 130), 8, 2, 16, 16, "bf16", "int8"),
 ]
 
 
@@ -45,7 +46,8 @@ def _logical_f64(wl, kind, idx, L):
     """Logical K/V of a stream in float64, without the oracle's codecs.
 
     fp8 uses torch's own float8_e4m3fn cast (after clamping, since torch's cast
-    does not saturate) and the per-head scale."""
+    does not saturate) and the per-head scale; int8 uses torch's per-channel
+    qint8 quantizer (round half to even of x / scale per head)."""
     k, v = wk.logical_kv(wl, kind, idx, L)
     s = wl.spec
     if s.kv_dtype == "bf16":
@@ -53,11 +55,23 @@ def _logical_f64(wl, kind, idx, L):
         return f(k), f(v)
     if s.kv_dtype == "f32":
         return torch.from_numpy(k).double(), torch.from_numpy(v).double()
+    if s.kv_dtype == "int8":
+        return (_torch_int8(k, wl.k_scale).double() * torch.from_numpy(wl.k_scale).double()[None, :, None],
+                _torch_int8(v, wl.v_scale).double() * torch.from_numpy(wl.v_scale).double()[None, :, None])
     def q8(x, sc):
         sc = torch.from_numpy(sc).float()[None, :, None]
         y = (torch.from_numpy(x).float() / sc).clamp(-448, 448)
         return y.to(torch.float8_e4m3fn).double() * sc.double()
     return q8(k, wl.k_scale), q8(v, wl.v_scale)
+
+
+def _torch_int8(x, sc):
+    """Codes [L][Hkv][D] from torch's per-channel qint8 quantizer (channel =
+    KV head, zero point 0)."""
+    q = torch.quantize_per_channel(torch.from_numpy(np.ascontiguousarray(x)),
+                                   torch.from_numpy(sc).double(), torch.zeros(len(sc), dtype=torch.long),
+                                   1, torch.qint8)
+    return q.int_repr()
 
 
 def _q_f64(x, dtype):
@@ -259,6 +273,8 @@ def test_append_places_rows_and_keeps_poison(case):
                 y = (torch.from_numpy(x) / torch.from_numpy(sc)[None, :, None]).clamp(-448, 448)
                 return y.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
             kl, vl = q8(kl, wl.k_scale), q8(vl, wl.v_scale)
+        if s.kv_dtype == "int8":
+            kl, vl = _torch_int8(kl, wl.k_scale).numpy(), _torch_int8(vl, wl.v_scale).numpy()
         assert kg.tobytes() == np.ascontiguousarray(kl).tobytes()
         assert vg.tobytes() == np.ascontiguousarray(vl).tobytes()
         for t in range(L):
@@ -334,3 +350,13 @@ def test_planted_fp8_mistake_is_caught(monkeypatch):
     monkeypatch.setattr(oa, "f32_to_e4m3fn", truncating)
     with pytest.raises(AssertionError):
         test_append_places_rows_and_keeps_poison(SMALL[3])
+
+
+def test_planted_int8_mistake_is_caught(monkeypatch):
+    def truncating(q):                # round toward zero instead of half to even
+        q = np.asarray(q, np.float32).astype(np.float64)
+        return np.clip(np.trunc(np.nan_to_num(q)), -127, 127).astype(np.int8)
+    monkeypatch.setattr(oa, "f32_to_int8_sym", truncating)
+    with pytest.raises(AssertionError):
+        test_append_places_rows_and_keeps_poison(SMALL[-1])
+

@@ -112,3 +112,55 @@ def test_bf16_decode_vs_torch():
     nan = np.isnan(ref)
     assert np.array_equal(np.isnan(ours), nan)
     assert np.array_equal(ours[~nan], ref[~nan])
+
+
+# ------------------------------------------------------------------ int8 ----
+def test_int8_exact_multiples_and_ties():
+    """Symmetric int8 codes: integers map to themselves, ties go to the even
+    neighbour (round half to even), at a power-of-two scale where x / scale
+    is exact."""
+    k = np.arange(-127, 128)
+    scale = np.float32(2.0 ** -3)
+    x = (k * 2.0 ** -3).astype(np.float32)
+    assert np.array_equal(formats.f32_to_int8_sym(x / scale), k.astype(np.int8))
+    q = np.array([0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 125.5, -126.5], dtype=np.float32)
+    want = np.array([0, 2, 2, 0, -2, -2, 126, -126], dtype=np.int8)
+    assert np.array_equal(formats.f32_to_int8_sym(q), want)
+
+
+def test_int8_saturation_and_special_values():
+    q = np.array([127.49, 127.5, 128.0, 1e30, np.inf, -127.5, -128.0, -np.inf, np.nan, -0.0],
+                 dtype=np.float32)
+    want = np.array([127, 127, 127, 127, 127, -127, -127, -127, 0, 0], dtype=np.int8)
+    assert np.array_equal(formats.f32_to_int8_sym(q), want)
+    rng = np.random.default_rng(3)
+    codes = formats.f32_to_int8_sym(rng.normal(0, 300, 100000).astype(np.float32))
+    assert codes.min() == -127 and codes.max() == 127     # -128 is never produced
+
+
+def test_int8_encode_vs_torch_quantize_per_tensor():
+    """torch's per-tensor qint8 quantizer (round half to even of x * (1/scale),
+    zero point 0) on values inside +-126 code steps, at a power-of-two scale
+    (where x * (1/scale) equals x / scale exactly)."""
+    rng = np.random.default_rng(5)
+    scale = 2.0 ** -5
+    x = (rng.uniform(-126, 126, 200000) * scale).astype(np.float32)
+    x[:505] = (np.arange(-252, 253) * 0.5 * scale).astype(np.float32)       # ties within +-126
+    ref = torch.quantize_per_tensor(torch.from_numpy(x), scale, 0, torch.qint8).int_repr()
+    ours = formats.f32_to_int8_sym(x / np.float32(scale))
+    assert np.array_equal(ours, ref.numpy())
+
+
+def test_int8_round_trip_error_bound():
+    """|c * scale - x| <= scale * (1/2 + 2^-18) inside the range (the
+    quotient x / scale is first rounded to float32: half an ulp, at most
+    2^-18 code steps below 128); beyond it the error is |x| - 127 * scale."""
+    rng = np.random.default_rng(6)
+    scale = np.float32(0.0371)
+    x = rng.normal(0, 3, 100000).astype(np.float32)
+    c = formats.f32_to_int8_sym(x / scale)
+    back = formats.int8_to_f64(c) * np.float64(scale)
+    inside = np.abs(x.astype(np.float64)) <= 127 * np.float64(scale)
+    err = np.abs(back - x.astype(np.float64))
+    assert err[inside].max() <= np.float64(scale) * (0.5 + 2.0 ** -18)
+    assert np.allclose(err[~inside], np.abs(x[~inside].astype(np.float64)) - 127 * np.float64(scale))
