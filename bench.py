@@ -125,6 +125,84 @@ def copy_calibration(args) -> int:
     return 0
 
 
+def chunk_sweep(args) -> int:
+    """Prefill of long prompts in chunks of several sizes (P1 §5.3 leaves the
+    chunk size to experiment) against one context-attention call over the
+    whole prompts' contiguous K/V.  8B-shaped GQA (32/8 heads, head_dim 128,
+    page 32), 4 prompts of 8192 tokens, bf16, seeded N(0,1) data.  Each chunk
+    step appends the chunk's K/V and runs one chunked-prefill call for all
+    four prompts; the sweep line reports the summed time per chunk size."""
+    import torch
+
+    from paged_kv_cache_277_amd import binding as B
+    from paged_kv_cache_277_amd import device as dev
+    from paged_kv_cache_277_amd import workloads as wk
+
+    R, L, Hq, Hkv, D, P = 4, 8192, 32, 8, 128, 32
+    scale = 1.0 / np.sqrt(D)
+    rng = np.random.default_rng(20261202)
+    T = R * L
+    q = dev._dev(wk.bf16_bits_rne(rng.standard_normal((T, Hq, D), dtype=np.float32)), "bf16", "cuda")
+    k = dev._dev(wk.bf16_bits_rne(rng.standard_normal((T, Hkv, D), dtype=np.float32)), "bf16", "cuda")
+    v = dev._dev(wk.bf16_bits_rne(rng.standard_normal((T, Hkv, D), dtype=np.float32)), "bf16", "cuda")
+    npg = L // P
+    perm = rng.permutation(R * npg).astype(np.int32)
+    bt = torch.from_numpy(perm.reshape(R, npg).copy()).cuda()
+    cache = B.PagedCache(dev.poisoned_pool(R * npg, Hkv, P, D, "bf16", "cuda"),
+                         dev.poisoned_pool(R * npg, Hkv, P, D, "bf16", "cuda"))
+    flops = 4 * Hq * D * R * (L * (L + 1) // 2)
+    qv = q.view(R, L, Hq, D)
+    kv_, vv_ = k.view(R, L, Hkv, D), v.view(R, L, Hkv, D)
+    results = []
+
+    def timed(fn, reps):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    for C in (256, 512, 1024, 2048, 4096, 8192):
+        steps = []
+        for pos in range(0, L, C):
+            c = min(C, L - pos)
+            sq = qv[:, pos:pos + c].contiguous().view(R * c, Hq, D)
+            sk = kv_[:, pos:pos + c].contiguous().view(R * c, Hkv, D)
+            sv = vv_[:, pos:pos + c].contiguous().view(R * c, Hkv, D)
+            cu = torch.arange(0, R * c + 1, c, dtype=torch.int32, device="cuda")
+            ctx = torch.full((R,), pos, dtype=torch.int32, device="cuda")
+            out = torch.empty_like(sq)
+            ws = B.prefill_workspace(cache, R, R * c, Hq, c, pos + c)
+            steps.append((sq, sk, sv, cu, ctx, out, ws, c, pos + c))
+
+        def run():
+            for sq, sk, sv, cu, ctx, out, ws, c, tot in steps:
+                B.pkv_kv_cache_append(cache, sk, sv, cu, ctx, bt)
+                B.pkv_paged_attn_chunked_prefill(cache, sq, out, cu, ctx, bt, c, tot, scale,
+                                                 workspace=ws)
+        ms = timed(run, args.steps)
+        results.append({"chunk": C, "steps": len(steps), "ms": round(ms, 3),
+                        "tflops": round(flops / ms / 1e9, 1)})
+        print(f"[sweep] chunk {C}: {ms:.3f} ms", file=sys.stderr, flush=True)
+        del steps
+    out = torch.empty_like(q)
+    cu = torch.arange(0, T + 1, L, dtype=torch.int32, device="cuda")
+    ws = B.context_workspace(R, T, Hq, Hkv, D, L)
+    ms = timed(lambda: B.pkv_context_fmha(q, k, v, out, cu, L, scale, workspace=ws), args.steps)
+    print(json.dumps({"chunk_sweep": results,
+                      "context_fmha": {"ms": round(ms, 3), "tflops": round(flops / ms / 1e9, 1)},
+                      "config": {"workload": "prefill of 4 x 8192-token prompts, 32/8 heads, "
+                                             "head_dim 128, page 32, bf16",
+                                 "causal_gflop": round(flops / 1e9, 1)},
+                      "mfma_peak_tflops": MFMA_BF16_PEAK_TFS}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -142,6 +220,9 @@ def main() -> int:
                     help="mixed_step: one pkv_mixed_step call per step, prefill on a second "
                          "stream; calls: append, decode and prefill calls one after another; "
                          "graph / graph_mixed_step: replays of those captured as a HIP graph")
+    ap.add_argument("--chunk-sweep", action="store_true",
+                    help="instead of the step benchmark: chunked prefill of long prompts at "
+                         "several chunk sizes against one context-attention call")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain device copy of known size instead (counter scaling)")
     args = ap.parse_args()
@@ -160,6 +241,8 @@ def main() -> int:
     torch.cuda.set_device(0)
     if args.copy_calibration:
         return copy_calibration(args)
+    if args.chunk_sweep:
+        return chunk_sweep(args)
     spec = (wk.variant(f"{args.workload}-{args.kv_format}") if args.kv_format
             else wk.CONFIGS[args.workload])
     t0 = time.perf_counter()

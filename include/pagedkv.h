@@ -292,6 +292,40 @@ size_t pkv_prefill_workspace_bytes(const pkv_cache_desc* cache, int32_t num_reqs
                                    int32_t split_tokens);
 
 /* ------------------------------------------------------------------------ *
+ * context_fmha — causal attention of whole prompts over their own contiguous
+ * K/V, no pages (the fused multi-head attention of a context phase:
+ * "TensorRT-LLM性能调优：提升LLM推理效率", layer fusion, fused MHA = scaled
+ * dot-product attention with a causal mask; the context_fmha build option of
+ * "如何用TensorRT-LLM和Triton Server实现LLM的高效推理？…" §2; the FMHA plugin of
+ * "4. TensorRT-LLM架构与核心组件…" §4.3).  Token i of sequence s attends tokens
+ * 0..i of s.  The same kernel as chunked prefill with K/V addressed directly,
+ * key ranges and merge included.
+ *
+ * q, out     : device bf16 packed [num_tokens][num_q_heads][head_dim]
+ * k, v       : device bf16 packed [num_tokens][num_kv_heads][head_dim]
+ * dtype      : PKV_BF16 (the only supported type)
+ * lse        : device float[num_tokens][num_q_heads] or NULL
+ * cu_seqlens : device int32[num_seqs+1], cu[0] = 0, every length <= max_seqlen,
+ *              cu[num_seqs] = num_tokens
+ * split_tokens, workspace: as for pkv_paged_attn_chunked_prefill, with
+ *              max_seqlen in place of max_total_len.
+ * head_dim 64 or 128, num_q_heads a multiple of num_kv_heads, group <= 16.
+ * ------------------------------------------------------------------------ */
+pkv_status pkv_context_fmha(const void* q, const void* k, const void* v, int32_t dtype, void* out,
+                            float* lse, const int32_t* cu_seqlens, int32_t num_seqs,
+                            int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t max_seqlen, float sm_scale,
+                            int32_t split_tokens, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/* Workspace bytes of a context_fmha call (0: one key range, none needed;
+ * also 0 on invalid arguments). */
+size_t pkv_context_fmha_workspace_bytes(int32_t num_seqs, int32_t num_tokens,
+                                        int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t max_seqlen,
+                                        int32_t split_tokens);
+
+/* ------------------------------------------------------------------------ *
  * mixed_step — one in-flight batching step in one call: new tokens join the
  * cache, then decode sequences and prefill chunks attend it
  * ("TensorRT-LLM内核融合与动态批处理", In-flight Batching: requests at different

@@ -171,6 +171,32 @@ def paged_attn_chunked_prefill(q: np.ndarray, q_dtype: str, k_pool: np.ndarray,
     return out, lse
 
 
+# ------------------------------------------------- context attention -------
+def context_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, dtype: str,
+                      cu_seqlens: np.ndarray, sm_scale: float,
+                      rows: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Causal attention of whole prompts over their own contiguous K/V
+    (fused MHA with a causal mask, "TensorRT-LLM性能调优：提升LLM推理效率"; the
+    context_fmha path of "如何用TensorRT-LLM和Triton Server实现LLM的高效推理？…" §2).
+
+    Packed q [T][Hq][D], k/v [T][Hkv][D]; sequence s owns rows
+    cu_seqlens[s] .. cu_seqlens[s+1]-1, and its token i attends its tokens
+    0..i.  Returns float64 (out, lse) for the packed rows ``rows`` (all by
+    default)."""
+    T, Hq, D = q.shape
+    if rows is None:
+        rows = np.arange(T)
+    seq_of = np.searchsorted(cu_seqlens, np.arange(T), side="right") - 1
+    out = np.zeros((len(rows), Hq, D))
+    lse = np.zeros((len(rows), Hq))
+    for n, t in enumerate(rows):
+        c0 = int(cu_seqlens[int(seq_of[t])])
+        kk = storage_to_f64(k[c0:t + 1], dtype)
+        vv = storage_to_f64(v[c0:t + 1], dtype)
+        out[n], lse[n] = attend(storage_to_f64(q[t], dtype), kk, vv, sm_scale)
+    return out, lse
+
+
 # ----------------------------------------------------- split + merge -------
 def split_partials(q: np.ndarray, k: np.ndarray, v: np.ndarray, sm_scale: float,
                    split: int):

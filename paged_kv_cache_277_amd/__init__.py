@@ -11,4 +11,4 @@ from .binding import (PagedCache, PageAllocator, PkvError, Scheduler, decode_wor
                       pkv_paged_attn_decode, pkv_paged_attn_decode_partial,
                       pkv_prefill_split_tokens, pkv_prefill_workspace_bytes, prefill_workspace,
                       pkv_validate_block_tables, pkv_mixed_step, append_batch,
-                      decode_batch, prefill_batch)
+                      decode_batch, prefill_batch, pkv_context_fmha, context_workspace)

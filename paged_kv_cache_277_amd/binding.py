@@ -116,6 +116,9 @@ _SIGS = {
     "pkv_prefill_split_tokens": (_I, [_P, _I, _I, _I, _I]),
     "pkv_prefill_workspace_bytes": (_SZ, [_P, _I, _I, _I, _I, _I, _I]),
     "pkv_mixed_step": (_I, [_P, _P, _P, _P, _F, _P, _P]),
+    "pkv_context_fmha": (_I, [_P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P,
+                              _SZ, _P]),
+    "pkv_context_fmha_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
     "pkv_validate_block_tables": (_I, [_P, _P, _I, _P, _I, _P]),
     "pkv_sched_create": (_I, [_P, C.POINTER(C.c_void_p)]),
     "pkv_sched_destroy": (None, [_P]),
@@ -493,6 +496,36 @@ def pkv_paged_attn_chunked_prefill(cache: PagedCache, q: torch.Tensor, out: torc
         cache.desc, _ptr(q), _code_of(q), _ptr(out), _code_of(out), _ptr(lse), _ptr(cu_q_lens),
         _ptr(ctx_before), _ptr(block_tables), block_tables.shape[1], R, q.shape[0], q.shape[1],
         max_chunk_len, max_total_len, float(sm_scale), split_tokens, wp, wb, _stream(stream)))
+
+
+def context_workspace(num_seqs: int, num_tokens: int, num_q_heads: int, num_kv_heads: int,
+                      head_dim: int, max_seqlen: int, split_tokens: int = 0,
+                      device="cuda") -> Optional[torch.Tensor]:
+    n = lib().pkv_context_fmha_workspace_bytes(num_seqs, num_tokens, num_q_heads, num_kv_heads,
+                                               head_dim, max_seqlen, split_tokens)
+    return None if n == 0 else torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def pkv_context_fmha(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                     cu_seqlens: torch.Tensor, max_seqlen: int, sm_scale: float,
+                     lse: Optional[torch.Tensor] = None, split_tokens: int = 0,
+                     workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Causal attention of whole prompts over contiguous K/V (no pages)."""
+    _need(q.dim() == 3 and q.is_contiguous() and out.shape == q.shape and out.is_contiguous(),
+          "q / out must be contiguous [T][Hq][D]")
+    _need(k.dim() == 3 and k.shape == v.shape and k.is_contiguous() and v.is_contiguous()
+          and k.shape[0] == q.shape[0] and k.shape[2] == q.shape[2],
+          "k / v must be contiguous [T][Hkv][D] like q")
+    _need(q.dtype == k.dtype == v.dtype == out.dtype, "q, k, v and out share one dtype")
+    _i32(cu_seqlens, "cu_seqlens")
+    if lse is not None:
+        _need(lse.dtype == torch.float32 and lse.shape == q.shape[:2] and lse.is_contiguous(),
+              "lse must be float32 [T][Hq]")
+    wp, wb = _ws(workspace)
+    _check(lib().pkv_context_fmha(_ptr(q), _ptr(k), _ptr(v), _code_of(q), _ptr(out), _ptr(lse),
+                                  _ptr(cu_seqlens), cu_seqlens.shape[0] - 1, q.shape[0],
+                                  q.shape[1], k.shape[1], q.shape[2], max_seqlen,
+                                  float(sm_scale), split_tokens, wp, wb, _stream(stream)))
 
 
 def append_batch(k_new: torch.Tensor, v_new: torch.Tensor, cu_new_tokens: torch.Tensor,

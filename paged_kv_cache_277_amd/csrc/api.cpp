@@ -217,20 +217,89 @@ pkv_status prepare_decode(const pkv_cache_desc* cache, const void* q, int32_t q_
 // contexts differ widely — while shorter requests stay in one range and need
 // no merge.  Contexts of up to 1024 keys take one range.  F32 caches
 // (generic path) always take one range.
-int32_t default_prefill_split(const pkv_cache_desc* c, int32_t max_total) {
+int32_t split_for_keys(int32_t max_total, bool one_range) {
   const int32_t one = std::max<int32_t>(64, (max_total + 63) / 64 * 64);
-  if (c->kv_dtype == PKV_F32) return one;
+  if (one_range) return one;
   const int32_t part = (int32_t)(((int64_t)max_total * 3 / 5 + 63) / 64 * 64);
   return std::min<int32_t>(one, std::max<int32_t>(1024, part));
 }
 
-size_t prefill_ws_bytes(const pkv_cache_desc* c, int32_t num_q_tokens, int32_t num_q_heads,
-                        int32_t ms) {
+int32_t default_prefill_split(const pkv_cache_desc* c, int32_t max_total) {
+  return split_for_keys(max_total, c->kv_dtype == PKV_F32);
+}
+
+size_t ranges_ws_bytes(int32_t head_dim, int32_t num_q_tokens, int32_t num_q_heads, int32_t ms) {
   if (ms <= 1 || num_q_tokens <= 0) return 0;
   const size_t n = (size_t)num_q_tokens * num_q_heads * ms;
-  const size_t acc = (n * c->head_dim * 4 + 255) / 256 * 256;
+  const size_t acc = (n * head_dim * 4 + 255) / 256 * 256;
   const size_t ml = (n * 2 * 4 + 255) / 256 * 256;
   return acc + ml;
+}
+
+size_t prefill_ws_bytes(const pkv_cache_desc* c, int32_t num_q_tokens, int32_t num_q_heads,
+                        int32_t ms) {
+  return ranges_ws_bytes(c->head_dim, num_q_tokens, num_q_heads, ms);
+}
+
+// Host checks of a context-attention call (contiguous bf16 q/k/v); fills `a`
+// (pointers included when given) and *need_out with the workspace bytes.
+pkv_status prepare_context(const void* q, const void* k, const void* v, int32_t dtype, void* out,
+                           float* lse, const int32_t* cu_seqlens, int32_t num_seqs,
+                           int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t max_seqlen, float sm_scale,
+                           int32_t split_tokens, bool check_ptrs, pkv::AttnArgs* a,
+                           size_t* need_out) {
+  if (dtype != PKV_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, "context attention takes bf16 q/k/v/out (dtype %d)", dtype);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", head_dim);
+  if (num_kv_heads <= 0 || num_q_heads <= 0 || num_q_heads % num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID_ARG, "num_q_heads %d must be a positive multiple of num_kv_heads %d",
+                num_q_heads, num_kv_heads);
+  if (num_q_heads / num_kv_heads > 16)
+    return fail(PKV_ERR_UNSUPPORTED, "group size %d > 16", num_q_heads / num_kv_heads);
+  if (num_seqs < 0 || num_tokens < 0 || max_seqlen < 0 || split_tokens < 0)
+    return fail(PKV_ERR_INVALID_ARG, "negative size");
+  if (num_seqs > kMaxGridYZ) return fail(PKV_ERR_UNSUPPORTED, "num_seqs %d > %d", num_seqs, kMaxGridYZ);
+  if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f))
+    return fail(PKV_ERR_INVALID_ARG, "sm_scale must be finite and positive");
+  std::memset(a, 0, sizeof *a);
+  a->c.k_pool = k;
+  a->c.v_pool = v;
+  a->c.num_kv_heads = num_kv_heads;
+  a->c.head_dim = head_dim;
+  a->c.page_size = 16;
+  a->c.kv_dtype = PKV_BF16;
+  a->prefill = 1;
+  a->contiguous = 1;
+  a->num_rows = num_seqs;
+  a->num_tokens = num_tokens;
+  a->max_chunk = max_seqlen;
+  a->num_q_heads = num_q_heads;
+  a->max_splits = 1;
+  a->split_tokens = 64;
+  if (need_out) *need_out = 0;
+  if (num_seqs == 0 || num_tokens == 0) return PKV_OK;
+  if (max_seqlen <= 0) return fail(PKV_ERR_INVALID_ARG, "max_seqlen must be positive");
+  const int32_t split = split_tokens ? split_tokens : split_for_keys(max_seqlen, false);
+  if (split % 64 != 0)
+    return fail(PKV_ERR_INVALID_ARG, "split_tokens %d is not a positive multiple of 64", split);
+  const int32_t ms = ceil_div(max_seqlen, split);
+  if (ms > kMaxGridYZ) return fail(PKV_ERR_UNSUPPORTED, "%d key ranges per row", ms);
+  a->split_tokens = split;
+  a->max_splits = std::max(1, ms);
+  if (pkv::prefill_mfma_grid(*a) > 0x7FFFFFFFLL) return fail(PKV_ERR_UNSUPPORTED, "grid too large");
+  const size_t need = ranges_ws_bytes(head_dim, num_tokens, num_q_heads, a->max_splits);
+  if (need_out) *need_out = need;
+  if (!check_ptrs) return PKV_OK;
+  if (!q || !k || !v || !out || !cu_seqlens)
+    return fail(PKV_ERR_INVALID_ARG, "context attention pointers must not be NULL");
+  a->q = q;
+  a->out = out;
+  a->lse = lse;
+  a->cu_q = cu_seqlens;
+  a->sm_scale = sm_scale;
+  return PKV_OK;
 }
 
 // Shape checks shared by the prefill call and its planning functions; fills
@@ -579,6 +648,44 @@ pkv_status pkv_mixed_step(const pkv_cache_desc* cache, const pkv_append_batch* a
   if ((st = launch_decode_call(da, s)) != PKV_OK) return st;
   if ((st = hip_status(hipEventRecord(ev_join, side), "mixed_step: join")) != PKV_OK) return st;
   return hip_status(hipStreamWaitEvent(s, ev_join, 0), "mixed_step: join");
+}
+
+pkv_status pkv_context_fmha(const void* q, const void* k, const void* v, int32_t dtype, void* out,
+                            float* lse, const int32_t* cu_seqlens, int32_t num_seqs,
+                            int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t max_seqlen, float sm_scale,
+                            int32_t split_tokens, void* workspace, size_t workspace_bytes_in,
+                            void* stream) {
+  pkv::AttnArgs a;
+  size_t need = 0;
+  pkv_status st = prepare_context(q, k, v, dtype, out, lse, cu_seqlens, num_seqs, num_tokens,
+                                  num_q_heads, num_kv_heads, head_dim, max_seqlen, sm_scale,
+                                  split_tokens, true, &a, &need);
+  if (st != PKV_OK) return st;
+  if (num_seqs == 0 || num_tokens == 0) return PKV_OK;
+  if (need > 0 && (!workspace || workspace_bytes_in < need))
+    return fail(PKV_ERR_INVALID_ARG, "workspace of %zu bytes needed, %zu given", need,
+                workspace_bytes_in);
+  if (need > 0) {
+    char* w = static_cast<char*>(workspace);
+    const size_t n = (size_t)num_tokens * num_q_heads * a.max_splits;
+    a.ws_acc = reinterpret_cast<float*>(w);
+    a.ws_ml = reinterpret_cast<float*>(w + (n * head_dim * 4 + 255) / 256 * 256);
+  }
+  return launch_prefill_call(a, static_cast<hipStream_t>(stream));
+}
+
+size_t pkv_context_fmha_workspace_bytes(int32_t num_seqs, int32_t num_tokens,
+                                        int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t max_seqlen,
+                                        int32_t split_tokens) {
+  pkv::AttnArgs a;
+  size_t need = 0;
+  if (prepare_context(nullptr, nullptr, nullptr, PKV_BF16, nullptr, nullptr, nullptr, num_seqs,
+                      num_tokens, num_q_heads, num_kv_heads, head_dim, max_seqlen, 1.0f,
+                      split_tokens, false, &a, &need) != PKV_OK)
+    return 0;
+  return need;
 }
 
 pkv_status pkv_validate_block_tables(const pkv_cache_desc* cache, const int32_t* block_tables,

@@ -365,7 +365,7 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(AttnArgs a) {
     // Chunk row i of request r is packed row cu_q[r] + i, at absolute
     // position ctx_before[r] + i: it attends that many keys plus itself.
     const int r = blockIdx.z, i = blockIdx.x;
-    const int c0 = a.cu_q[r], c1 = a.cu_q[r + 1], pr = a.ctx_before[r];
+    const int c0 = a.cu_q[r], c1 = a.cu_q[r + 1], pr = a.ctx_before ? a.ctx_before[r] : 0;
     if (i >= c1 - c0) return;
     z = c0 + i;
     L = pr + i + 1;

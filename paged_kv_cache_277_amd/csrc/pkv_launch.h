@@ -50,6 +50,7 @@ struct AttnArgs {
   float* ws_acc;                 // [rows][Hq][max_splits][D]   (prefill rows: tokens)
   float* ws_ml;                  // [rows][Hq][max_splits][2]
   int32_t prefill;
+  int32_t contiguous;            // prefill over contiguous K/V [tokens][Hkv][D] (no pages)
   int32_t page_shift;            // log2(page_size)
 };
 

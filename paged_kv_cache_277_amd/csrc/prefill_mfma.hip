@@ -72,10 +72,13 @@ struct PfRegs {
   u32x4 v[PfShape<KVT, D>::PPT];
 };
 
-template <int KVT, int D>
+// K/V rows come from the pages (PAGED) or, for context attention over a
+// whole prompt, from contiguous packed [tokens][Hkv][D] arrays whose request
+// r starts at row c0.
+template <int KVT, int D, bool PAGED>
 __device__ __forceinline__ void pf_load(PfRegs<KVT, D>& r, const uint8_t* kp, const uint8_t* vp,
-                                        const int32_t* pages, int pg0, int t0, int kmax, int Hkv,
-                                        int j, int pshift) {
+                                        const int32_t* pages, int pg0, int c0, int t0, int kmax,
+                                        int Hkv, int j, int pshift) {
   // Every call issues the same loads: pieces past kmax (or past the tile)
   // read the first 16 bytes of the pools instead, and pf_store zeroes them.
   // A fixed load count keeps the waits for older tiles exact.
@@ -88,10 +91,15 @@ __device__ __forceinline__ void pf_load(PfRegs<KVT, D>& r, const uint8_t* kp, co
     const int tok = piece / PR, pc = piece % PR;
     const int t = t0 + tok;
     const bool ok = piece < S::PIECES && t < kmax;
-    const int page = ok ? pages[(t >> pshift) - pg0] : 0;
-    const size_t off = ok ? ((((size_t)page * Hkv + j) << pshift | (size_t)(t & pmask)) * S::ROWB) +
-                                (size_t)pc * 16
-                          : 0;
+    size_t off = 0;
+    if constexpr (PAGED) {
+      const int page = ok ? pages[(t >> pshift) - pg0] : 0;
+      off = ok ? ((((size_t)page * Hkv + j) << pshift | (size_t)(t & pmask)) * S::ROWB) +
+                     (size_t)pc * 16
+               : 0;
+    } else {
+      off = ok ? ((size_t)(c0 + t) * Hkv + j) * S::ROWB + (size_t)pc * 16 : 0;
+    }
     r.k[i] = ld16(kp + off);
     r.v[i] = ld16(vp + off);
   }
@@ -141,7 +149,7 @@ __device__ __forceinline__ void pf_store(PfRegs<KVT, D> r, uint8_t* kl, uint8_t*
 // The final (m, l, acc) describes the same softmax whichever shift was used.
 constexpr float kSlack = 8.0f;
 
-template <int KVT, int D>
+template <int KVT, int D, bool PAGED>
 __global__ __launch_bounds__(256, 2) void prefill_mfma(AttnArgs a, int nqb, int npg) {
   using S = PfShape<KVT, D>;
   constexpr int KK = D / 32, DT = D / 16;
@@ -167,7 +175,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma(AttnArgs a, int nqb, int 
   const int qb = nqb - 1 - qb_rev;               // later (heavier) query blocks first
   const int row0 = qb * kRows;                   // first flat row (token*G + head) of the block
   if (row0 >= C * G) return;
-  const int Pr = a.ctx_before[r];
+  const int Pr = PAGED ? a.ctx_before[r] : 0;    // a whole prompt has nothing cached before it
   const int last_row = min(C * G, row0 + kRows) - 1;
   const int kneed = Pr + last_row / G + 1;       // keys needed by the block's last row
   const int t_begin = rng * a.split_tokens;      // this workgroup's key range
@@ -220,7 +228,6 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma(AttnArgs a, int nqb, int 
     l[nt] = 0.0f;
   }
 
-  const int32_t* btrow = a.bt + (size_t)r * a.bt_stride;
   const uint8_t* kp = static_cast<const uint8_t*>(a.c.k_pool);
   const uint8_t* vp = static_cast<const uint8_t*>(a.c.v_pool);
   const int ntiles = (kmax - t_begin + kTile - 1) / kTile;
@@ -230,18 +237,21 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma(AttnArgs a, int nqb, int 
   // pf_load indexes them by absolute page number minus pg0.
   int32_t* pages = reinterpret_cast<int32_t*>(smem + 2 * S::STAGE);
   const int pg0 = t_begin >> pshift;
-  const int npages = ((kmax - 1) >> pshift) - pg0 + 1;
-  for (int i = threadIdx.x; i < npages; i += blockDim.x) pages[i] = btrow[pg0 + i];
-  __syncthreads();
+  if constexpr (PAGED) {
+    const int32_t* btrow = a.bt + (size_t)r * a.bt_stride;
+    const int npages = ((kmax - 1) >> pshift) - pg0 + 1;
+    for (int i = threadIdx.x; i < npages; i += blockDim.x) pages[i] = btrow[pg0 + i];
+    __syncthreads();
+  }
 
   // Pipeline: tile t is staged in register set t % 3 and LDS buffer t % 2.
   // While tile i is computed, the loads of tiles i+2 and i+3 are in flight
   // and tile i+1 (loaded two steps earlier) is written to the other LDS
   // buffer, so each load has two compute steps to land.
   PfRegs<KVT, D> r0, r1, r2;
-  pf_load<KVT, D>(r0, kp, vp, pages, pg0, t_begin, kmax, Hkv, j, pshift);
-  pf_load<KVT, D>(r1, kp, vp, pages, pg0, t_begin + kTile, kmax, Hkv, j, pshift);
-  pf_load<KVT, D>(r2, kp, vp, pages, pg0, t_begin + 2 * kTile, kmax, Hkv, j, pshift);
+  pf_load<KVT, D, PAGED>(r0, kp, vp, pages, pg0, c0, t_begin, kmax, Hkv, j, pshift);
+  pf_load<KVT, D, PAGED>(r1, kp, vp, pages, pg0, c0, t_begin + kTile, kmax, Hkv, j, pshift);
+  pf_load<KVT, D, PAGED>(r2, kp, vp, pages, pg0, c0, t_begin + 2 * kTile, kmax, Hkv, j, pshift);
   pf_store<KVT, D>(r0, smem, smem + kTile * S::K_LDS, t_begin, kmax);
   __syncthreads();
 
@@ -249,7 +259,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma(AttnArgs a, int nqb, int 
     const int t0 = t_begin + it * kTile;
     uint8_t* kl = smem + (it & 1) * S::STAGE;
     uint8_t* vl = kl + kTile * S::K_LDS;
-    pf_load<KVT, D>(rfree, kp, vp, pages, pg0, t0 + 3 * kTile, kmax, Hkv, j, pshift);
+    pf_load<KVT, D, PAGED>(rfree, kp, vp, pages, pg0, c0, t0 + 3 * kTile, kmax, Hkv, j, pshift);
 
     if (t0 < wave_kmax) {                        // skip tiles wholly above this wave's diagonal
       // ---- S^T for the two 16-key blocks; each K operand feeds every N-tile ----
@@ -380,10 +390,13 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma(AttnArgs a, int nqb, int 
 }  // namespace
 
 // The block-table slice of one key range must fit the LDS staging area: a
-// range of split_tokens keys touches at most split/page + 1 pages.
+// range of split_tokens keys touches at most split/page + 1 pages.  Context
+// attention (contiguous bf16 K/V) has no table.
 bool prefill_mfma_supported(const AttnArgs& a) {
-  return a.prefill && a.c.kv_dtype != KV_F32 && (a.c.head_dim == 64 || a.c.head_dim == 128) &&
-         a.split_tokens % kTile == 0 && (a.split_tokens >> a.page_shift) + 1 <= kMaxPages;
+  if (!a.prefill || (a.c.head_dim != 64 && a.c.head_dim != 128) || a.split_tokens % kTile != 0)
+    return false;
+  if (a.contiguous) return a.c.kv_dtype == KV_BF16;
+  return a.c.kv_dtype != KV_F32 && (a.split_tokens >> a.page_shift) + 1 <= kMaxPages;
 }
 
 long long prefill_mfma_grid(const AttnArgs& a) {
@@ -393,6 +406,12 @@ long long prefill_mfma_grid(const AttnArgs& a) {
   return (pairs + 7) / 8 * 8 * nqb * a.max_splits;
 }
 
+template <int KVT, bool PAGED>
+void launch_pf(const AttnArgs& a, dim3 grid, hipStream_t s, int nqb, int npg) {
+  if (a.c.head_dim == 128) hipLaunchKernelGGL((prefill_mfma<KVT, 128, PAGED>), grid, dim3(256), 0, s, a, nqb, npg);
+  else hipLaunchKernelGGL((prefill_mfma<KVT, 64, PAGED>), grid, dim3(256), 0, s, a, nqb, npg);
+}
+
 hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t s) {
   const int G = a.num_q_heads / a.c.num_kv_heads;
   const int nqb = (a.max_chunk * G + kRows - 1) / kRows;
@@ -400,17 +419,11 @@ hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t s) {
   const long long nwg = prefill_mfma_grid(a);
   if (nwg == 0) return hipSuccess;
   if (nwg > 0x7FFFFFFFLL) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)nwg), block(256);
-  if (a.c.kv_dtype == KV_BF16) {
-    if (a.c.head_dim == 128) hipLaunchKernelGGL((prefill_mfma<KV_BF16, 128>), grid, block, 0, s, a, nqb, npg);
-    else hipLaunchKernelGGL((prefill_mfma<KV_BF16, 64>), grid, block, 0, s, a, nqb, npg);
-  } else if (a.c.kv_dtype == KV_FP8) {
-    if (a.c.head_dim == 128) hipLaunchKernelGGL((prefill_mfma<KV_FP8, 128>), grid, block, 0, s, a, nqb, npg);
-    else hipLaunchKernelGGL((prefill_mfma<KV_FP8, 64>), grid, block, 0, s, a, nqb, npg);
-  } else {
-    if (a.c.head_dim == 128) hipLaunchKernelGGL((prefill_mfma<KV_INT8, 128>), grid, block, 0, s, a, nqb, npg);
-    else hipLaunchKernelGGL((prefill_mfma<KV_INT8, 64>), grid, block, 0, s, a, nqb, npg);
-  }
+  const dim3 grid((unsigned)nwg);
+  if (a.contiguous) launch_pf<KV_BF16, false>(a, grid, s, nqb, npg);
+  else if (a.c.kv_dtype == KV_BF16) launch_pf<KV_BF16, true>(a, grid, s, nqb, npg);
+  else if (a.c.kv_dtype == KV_FP8) launch_pf<KV_FP8, true>(a, grid, s, nqb, npg);
+  else launch_pf<KV_INT8, true>(a, grid, s, nqb, npg);
   return hipGetLastError();
 }
 

@@ -99,6 +99,10 @@ def test_allocator_threads():
 
 # ------------------------------------------------ host-side rejection -------
 FAKE = 0x1000  # never dereferenced: every call below fails its host checks first
+# With a GPU visible, a missing host check would launch a kernel on FAKE
+# pointers; these tests run only where no GPU is (the checks are host code).
+fake_ptrs = pytest.mark.skipif(torch.cuda.is_available(),
+                               reason="fake device pointers: host checks are tested without a GPU")
 
 
 def _desc(**kw):
@@ -115,6 +119,7 @@ def _decode(desc, q_dtype=B.PKV_BF16, out_dtype=B.PKV_BF16, Hq=4, max_len=64, st
                                          stride, FAKE, B_, Hq, max_len, scale, split, ws, wsb, None)
 
 
+@fake_ptrs
 @pytest.mark.parametrize("kw,status", [
     (dict(head_dim=96), B.PKV_ERR_UNSUPPORTED),
     (dict(page_size=8), B.PKV_ERR_UNSUPPORTED),
@@ -132,6 +137,7 @@ def test_decode_rejects_bad_cache(kw, status):
     assert B.lib().pkv_last_error()
 
 
+@fake_ptrs
 def test_decode_rejects_bad_arguments():
     d = _desc()
     assert _decode(d, Hq=3) == B.PKV_ERR_INVALID_ARG                 # 3 % 2 != 0
@@ -169,6 +175,7 @@ def test_workspace_and_split_planning():
     assert lib.pkv_decode_split_tokens(C.byref(d), 64, 41, 4096) == 0
 
 
+@fake_ptrs
 def test_append_and_prefill_reject_on_host():
     lib = B.lib()
     d = _desc()
@@ -242,6 +249,7 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
         B.lib()
 
 
+@fake_ptrs
 def test_mixed_step_checks_every_part_before_launching():
     lib = B.lib()
     d = _desc(num_pages=64)
@@ -266,3 +274,26 @@ def test_mixed_step_checks_every_part_before_launching():
                                    2, 8, 4, 4, 3, 0, None, 0)               # total < chunk
     assert lib.pkv_mixed_step(C.byref(d), C.byref(app), C.byref(good_dec), C.byref(bad_pre), 0.1,
                               None, None) == B.PKV_ERR_INVALID_ARG
+
+
+@fake_ptrs
+def test_context_fmha_rejects_on_host_and_plans_workspace():
+    lib = B.lib()
+
+    def call(dtype=B.PKV_BF16, R=2, T=8, Hq=4, Hkv=2, D=64, maxlen=4, split=0, ws=None, wsb=0,
+             scale=0.1):
+        return lib.pkv_context_fmha(FAKE, FAKE, FAKE, dtype, FAKE, None, FAKE, R, T, Hq, Hkv, D,
+                                    maxlen, scale, split, ws, wsb, None)
+    assert call(dtype=B.PKV_F32) == B.PKV_ERR_UNSUPPORTED
+    assert call(D=96) == B.PKV_ERR_UNSUPPORTED
+    assert call(Hq=5) == B.PKV_ERR_INVALID_ARG
+    assert call(Hq=34) == B.PKV_ERR_UNSUPPORTED                     # group 17
+    assert call(split=96) == B.PKV_ERR_INVALID_ARG               # not a multiple of 64
+    assert call(scale=float("inf")) == B.PKV_ERR_INVALID_ARG
+    assert call(maxlen=0) == B.PKV_ERR_INVALID_ARG
+    assert call(maxlen=200, split=64) == B.PKV_ERR_INVALID_ARG      # needs a workspace
+    assert b"workspace" in lib.pkv_last_error()
+    assert call(T=0) == B.PKV_OK                                     # nothing to do
+    assert lib.pkv_context_fmha_workspace_bytes(2, 8, 4, 2, 64, 200, 64) >= 8 * 4 * 4 * (64 + 2) * 4
+    assert lib.pkv_context_fmha_workspace_bytes(2, 8, 4, 2, 64, 200, 256) == 0
+    assert lib.pkv_context_fmha_workspace_bytes(2, 8, 5, 2, 64, 200, 0) == 0   # invalid

@@ -360,3 +360,49 @@ def test_planted_int8_mistake_is_caught(monkeypatch):
     with pytest.raises(AssertionError):
         test_append_places_rows_and_keeps_poison(SMALL[-1])
 
+
+
+# ------------------------------------------------- context attention -------
+def _context_inputs(lens, Hq, Hkv, D, seed):
+    rng = np.random.default_rng(seed)
+    T = int(sum(lens))
+    q = wk.bf16_bits_rne(rng.standard_normal((T, Hq, D), dtype=np.float32))
+    k = wk.bf16_bits_rne(rng.standard_normal((T, Hkv, D), dtype=np.float32))
+    v = wk.bf16_bits_rne(rng.standard_normal((T, Hkv, D), dtype=np.float32))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    return q, k, v, cu
+
+
+def test_context_attention_matches_library_causal_sdpa():
+    """Each sequence against torch SDPA with is_causal (float64)."""
+    lens, Hq, Hkv, D = (1, 9, 40), 8, 2, 32
+    q, k, v, cu = _context_inputs(lens, Hq, Hkv, D, 9)
+    out, lse = oa.context_attention(q, k, v, "bf16", cu, 0.2)
+    for s in range(len(lens)):
+        a, b = int(cu[s]), int(cu[s + 1])
+        qq = _q_f64(q[a:b], "bf16")
+        kk, vv = _q_f64(k[a:b], "bf16"), _q_f64(v[a:b], "bf16")
+        mask = torch.ones(b - a, b - a, dtype=torch.bool).tril()
+        ro, rl = _sdpa(qq, kk, vv, 0.2, mask=mask)
+        np.testing.assert_allclose(out[a:b], ro, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse[a:b], rl, rtol=0, atol=1e-12)
+
+
+def test_context_attention_is_prefill_with_nothing_cached():
+    """Identity: the whole prompt as one chunk over its pages (ctx_before = 0)
+    gives the same rows as attention over the contiguous K/V."""
+    lens, Hq, Hkv, D, P = (5, 33, 17), 4, 2, 16, 16
+    q, k, v, cu = _context_inputs(lens, Hq, Hkv, D, 10)
+    out, lse = oa.context_attention(q, k, v, "bf16", cu, 0.25)
+    pages = [-(-n // P) for n in lens]
+    kp = np.zeros((sum(pages), Hkv, P, D), np.uint16)
+    vp = np.zeros_like(kp)
+    bt = np.full((len(lens), max(pages)), -1, np.int32)
+    nxt = 0
+    for s, n in enumerate(pages):
+        bt[s, :n] = np.arange(nxt, nxt + n)[::-1]          # any page order
+        nxt += n
+    ctx = np.zeros(len(lens), np.int32)
+    oa.kv_cache_append(kp, vp, "bf16", k, v, "bf16", cu, ctx, bt)
+    pout, plse = oa.paged_attn_chunked_prefill(q, "bf16", kp, vp, "bf16", cu, ctx, bt, 0.25)
+    assert np.array_equal(out, pout) and np.array_equal(lse, plse)
