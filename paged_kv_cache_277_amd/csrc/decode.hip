@@ -78,7 +78,7 @@ template <> __device__ __forceinline__ void store_o<uint16_t>(void* o, size_t i,
 }
 
 // Resolve which query row, context length and block-table row a launch row
-// (blockIdx.z) stands for.  Returns false if the row is empty padding.
+// (blockIdx.y) stands for.  Returns false if the row is empty padding.
 __device__ __forceinline__ bool resolve_row(const AttnArgs& a, int z, int& L, int& btr,
                                             size_t& qrow) {
   if (a.prefill) {
@@ -130,24 +130,31 @@ __global__ __launch_bounds__(256) void decode_partial_vec(AttnArgs a) {
 
   // KV heads are the fastest grid dimension: workgroups dispatched together
   // read the head slabs of the same physical pages, which sit side by side.
-  const int j = blockIdx.x, split = blockIdx.y, z = blockIdx.z;
+  // The slowest dimension counts ranges back from each row's last: the last
+  // (partial, on average half-size) range of every row is dispatched last,
+  // so the launch ends on short work items instead of full ones.
+  const int j = blockIdx.x, z = blockIdx.y;
   int L, btr;
   size_t qrow;
   if (!resolve_row(a, z, L, btr, qrow)) return;
   const int Hq = a.num_q_heads, Hkv = a.c.num_kv_heads;
   const int pshift = a.page_shift, pmask = (1 << pshift) - 1;
   const int G = Hq / Hkv;
-  const int t_begin = split * a.split_tokens;
-  if (t_begin >= L) {
-    if (split == 0) {  // empty context: output 0, lse = -inf
+  if (L <= 0) {
+    if (blockIdx.z == a.max_splits - 1) {  // empty context: output 0, lse = -inf
       for (int i = threadIdx.x; i < G * D; i += blockDim.x)
         store_o<QT>(a.out, (qrow * Hq + (size_t)j * G) * D + i, 0.0f);
       if (a.lse && threadIdx.x < G) a.lse[qrow * Hq + (size_t)j * G + threadIdx.x] = -INFINITY;
     }
     return;
   }
+  // (a length beyond max_splits ranges breaks the call's precondition: the
+  // clamp keeps every write inside the workspace)
+  const int n_split = min((L + a.split_tokens - 1) / a.split_tokens, a.max_splits);
+  const int split = n_split - a.max_splits + (int)blockIdx.z;
+  if (split < 0) return;
+  const int t_begin = split * a.split_tokens;
   const int t_end = min(L, t_begin + a.split_tokens);
-  const int n_split = (L + a.split_tokens - 1) / a.split_tokens;
 
   const int lane = threadIdx.x & 63;
   const int w = uniform(threadIdx.x >> 6);
@@ -433,7 +440,7 @@ hipError_t launch_vec_any(const AttnArgs& a, dim3 grid, hipStream_t s) {
 hipError_t launch_decode_partial(const AttnArgs& a, hipStream_t s) {
   if (a.num_rows == 0) return hipSuccess;
   if (decode_mfma_supported(a)) return launch_decode_partial_mfma(a, s);
-  const dim3 grid(a.c.num_kv_heads, a.max_splits, a.num_rows);
+  const dim3 grid(a.c.num_kv_heads, a.num_rows, a.max_splits);
   return launch_vec_any(a, grid, s);
 }
 
@@ -461,7 +468,7 @@ hipError_t launch_lse_merge(const AttnArgs& a, hipStream_t s) {
 hipError_t launch_prefill(const AttnArgs& a, hipStream_t s) {
   if (a.num_rows == 0 || a.max_chunk == 0) return hipSuccess;
   if (prefill_mfma_supported(a)) return launch_prefill_mfma(a, s);
-  const dim3 grid(a.c.num_kv_heads, 1, a.num_rows * a.max_chunk);
+  const dim3 grid(a.c.num_kv_heads, a.num_rows * a.max_chunk, 1);
   return launch_vec_any(a, grid, s);
 }
 

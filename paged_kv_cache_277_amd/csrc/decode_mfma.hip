@@ -130,22 +130,26 @@ __global__ __launch_bounds__(256, 2) void decode_partial_mfma(AttnArgs a) {
   __shared__ __attribute__((aligned(16)))
   uint8_t smem[STAGE_BYTES > MERGE_BYTES ? STAGE_BYTES : MERGE_BYTES];
 
-  const int j = blockIdx.x, split = blockIdx.y, z = blockIdx.z;
+  // Grid (KV head, row, range counted back from the row's last): the last,
+  // partial range of every row is dispatched last (see decode.hip).
+  const int j = blockIdx.x, z = blockIdx.y;
   const int L = a.context_lens[z];
   const int Hq = a.num_q_heads, Hkv = a.c.num_kv_heads;
   const int G = Hq / Hkv;
-  const int t_begin = split * a.split_tokens;
   const size_t qrow = (size_t)z;
-  if (t_begin >= L) {
-    if (split == 0) {
+  if (L <= 0) {
+    if (blockIdx.z == a.max_splits - 1) {  // empty context: output 0, lse = -inf
       for (int i = threadIdx.x; i < G * D; i += blockDim.x)
         static_cast<uint16_t*>(a.out)[(qrow * Hq + (size_t)j * G) * D + i] = 0;
       if (a.lse && threadIdx.x < G) a.lse[qrow * Hq + (size_t)j * G + threadIdx.x] = -INFINITY;
     }
     return;
   }
+  const int n_split = min((L + a.split_tokens - 1) / a.split_tokens, a.max_splits);
+  const int split = n_split - a.max_splits + (int)blockIdx.z;
+  if (split < 0) return;
+  const int t_begin = split * a.split_tokens;
   const int t_end = min(L, t_begin + a.split_tokens);
-  const int n_split = (L + a.split_tokens - 1) / a.split_tokens;
   const int lane = threadIdx.x & 63;
   const int w = uniform(threadIdx.x >> 6);
   const int g4 = lane >> 4, h = lane & 15;       // lane group and head slot
@@ -386,7 +390,7 @@ bool decode_mfma_supported(const AttnArgs& a) {
 }
 
 hipError_t launch_decode_partial_mfma(const AttnArgs& a, hipStream_t s) {
-  const dim3 grid(a.c.num_kv_heads, a.max_splits, a.num_rows), block(256);
+  const dim3 grid(a.c.num_kv_heads, a.num_rows, a.max_splits), block(256);
   if (a.c.kv_dtype == KV_BF16) {
     if (a.c.head_dim == 128) hipLaunchKernelGGL((decode_partial_mfma<KV_BF16, 128>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((decode_partial_mfma<KV_BF16, 64>), grid, block, 0, s, a);
