@@ -218,14 +218,19 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma(AttnArgs a, int nqb, int 
     for (int kk = 0; kk < KK; ++kk) settle(qb_reg[nt][kk]);
   }
 
+  // Row sums l come from the matrix cores too: an all-ones A operand times
+  // P^T gives sum_t P[row][t] in every element of the row's lanes — from the
+  // same bf16 P that multiplies V, with no VALU adds or cross-lane sums.
   f32x4 o[kNt][DT];
-  float m[kNt], l[kNt];
+  f32x4 lsum[kNt];
+  float m[kNt];
+  const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};   // bf16 1.0 pairs
 #pragma unroll
   for (int nt = 0; nt < kNt; ++nt) {
 #pragma unroll
     for (int i = 0; i < DT; ++i) o[nt][i] = f32x4{0, 0, 0, 0};
     m[nt] = -INFINITY;
-    l[nt] = 0.0f;
+    lsum[nt] = f32x4{0, 0, 0, 0};
   }
 
   const uint8_t* kp = static_cast<const uint8_t*>(a.c.k_pool);
@@ -308,7 +313,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma(AttnArgs a, int nqb, int 
           const float mn = fmaxf(m[nt], mx * smul);
           // (a row still at -inf has l = 0 and O = 0: any finite factor will do)
           const float alpha = m[nt] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m[nt] - mn);
-          l[nt] *= alpha;
+          lsum[nt] *= alpha;
 #pragma unroll
           for (int i = 0; i < DT; ++i) o[nt][i] *= alpha;
           m[nt] = mn;
@@ -318,12 +323,12 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma(AttnArgs a, int nqb, int 
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           p[i] = __builtin_amdgcn_exp2f(fmaf(sv[i], smul, -msub));
-          l[nt] += p[i];
         }
         pb[nt][0] = pack_bf16x2(p[0], p[1]);
         pb[nt][1] = pack_bf16x2(p[2], p[3]);
         pb[nt][2] = pack_bf16x2(p[4], p[5]);
         pb[nt][3] = pack_bf16x2(p[6], p[7]);
+        lsum[nt] = mfma16(ones, pb[nt], lsum[nt]);
       }
       // ---- O^T += V^T P^T; each V^T operand feeds every N-tile ----
       const int rd_row0 = 4 * g4 + (n >> 2);
@@ -355,15 +360,13 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma(AttnArgs a, int nqb, int 
     if (it + 2 < ntiles) step(it + 2, r2, r0);
   }
 
-  // ---- finish rows: l is split over the 4 lanes of a row.  A row whose
+  // ---- finish rows.  A row whose
   // keys fit one range (L <= split_tokens) is final here; otherwise this
   // range's (m, l, acc) goes to the workspace for the merge, if the row has
   // keys in it. ----
 #pragma unroll
   for (int nt = 0; nt < kNt; ++nt) {
-    float lt = l[nt];
-    lt += __shfl_xor(lt, 16, 64);
-    lt += __shfl_xor(lt, 32, 64);
+    const float lt = lsum[nt][0];
     const int L = my_lim[nt] + 1;                // keys this row attends
     const bool single = L <= a.split_tokens;     // all of them in range 0
     if (row_ok[nt] && single && rng == 0) {
