@@ -286,19 +286,48 @@ def main() -> int:
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / K
-    if args.launch != "calls":
-        # The kernel's own duration cannot be bracketed inside a replay or a
-        # fused call: time it in a short eager loop after the timed steps.
-        for i in range(K):
-            dw.append_step()
-            if wl.num_seqs:
+    # Kernel durations: the decode partial (and the prefill call) timed alone
+    # with events in an eager loop after the timed steps (inside a replay or a
+    # fused call they cannot be bracketed; with --launch calls the partial's
+    # events were recorded inside the timed loop already).
+    ev_pf = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(K)]
+    for i in range(K):
+        dw.append_step()
+        if wl.num_seqs:
+            if args.launch != "calls":
                 ev[i][0].record()
-                dw.decode_partial()
+            dw.decode_partial()
+            if args.launch != "calls":
                 ev[i][1].record()
-                dw.merge()
-            dw.prefill()
+            dw.merge()
+        ev_pf[i][0].record()
+        dw.prefill()
+        ev_pf[i][1].record()
+    torch.cuda.synchronize()
+    part_times = [a.elapsed_time(b) for a, b in ev] if wl.num_seqs else [0.0]
+    part_ms = float(np.mean(part_times))
+    pf_times = [a.elapsed_time(b) for a, b in ev_pf] if wl.num_prefill else []
+
+    # Cold-cache steps: a 1 GiB device write before each step (outside the
+    # events) evicts L2 and the Infinity Cache; median / p10 / p90 reported.
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    cold = []
+    for i in range(min(K, 20)):
+        flush.fill_(i & 0xFF)
         torch.cuda.synchronize()
-    part_ms = float(np.mean([a.elapsed_time(b) for a, b in ev])) if wl.num_seqs else 0.0
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        if graph is not None:
+            graph.replay()
+        elif side is not None:
+            dw.mixed_step(side_stream=side)
+        else:
+            dw.step()
+        b.record()
+        torch.cuda.synchronize()
+        cold.append(a.elapsed_time(b))
+    del flush
 
     dec_bytes = wk.decode_bytes(spec, wl.context_lens) if wl.num_seqs else 0
     e_in = wk.DTYPE_BYTES[spec.kv_in_dtype]
@@ -311,6 +340,7 @@ def main() -> int:
     step_bytes = dec_bytes + app_bytes + pf_bytes
     value = step_bytes / (ms * 1e-3) / 1e9
     part_gbs = dec_bytes / (part_ms * 1e-3) / 1e9 if part_ms > 0 else 0.0
+    cold_med = float(np.median(cold))
 
     line = {
         "metric": "paged decode attention: achieved HBM GB/s (% of peak) + seq-steps/s at 1 GPU",
@@ -334,17 +364,33 @@ def main() -> int:
                    "prefill_split_tokens": dw.pf["split"] if dw.pf else None,
                    "parallelism": "single GPU",
                    "launch": args.launch},
-        "seq_steps_per_s": round(wl.num_seqs / (ms * 1e-3), 1),
+        "seq_steps_per_s": round((wl.num_seqs + wl.num_prefill) / (ms * 1e-3), 1),
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "step_bytes": step_bytes,
+        "cold_cache": {"ms_median": round(cold_med, 5),
+                       "ms_p10": round(float(np.percentile(cold, 10)), 5),
+                       "ms_p90": round(float(np.percentile(cold, 90)), 5),
+                       "gbs_at_median": round(step_bytes / (cold_med * 1e-3) / 1e9, 2),
+                       "steps": len(cold), "flush_bytes": 1 << 30},
         "roofline": {"bound": "hbm", "kernel": "decode_partial", "achieved": round(part_gbs, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(part_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(spec.name),
-                     "kernel_ms": round(part_ms, 5), "bytes_per_launch": dec_bytes},
+                     "kernel_ms": round(part_ms, 5),
+                     "kernel_ms_p10_p50_p90": [round(float(np.percentile(part_times, q)), 5)
+                                               for q in (10, 50, 90)],
+                     "bytes_per_launch": dec_bytes},
     }
+    if spec.shared_prefix_pages and wl.num_seqs:
+        line["logical_step_bytes"] = (wk.decode_bytes(spec, wl.context_lens, unique_prefix=False)
+                                      + app_bytes)
     if flops:
+        pf_med = float(np.median(pf_times))
         line["prefill_flops"] = flops
+        line["prefill"] = {"flops": flops, "call_ms_median": round(pf_med, 5),
+                           "tflops": round(flops / (pf_med * 1e-3) / 1e12, 1),
+                           "mfma_frac": round(flops / (pf_med * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4),
+                           "note": "kernel plus its range merge, timed alone"}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
     print(json.dumps(line), flush=True)
