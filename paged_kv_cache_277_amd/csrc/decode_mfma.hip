@@ -37,6 +37,8 @@
 // current tile is computed.  Scores are kept in the log2 domain.
 #include <math.h>
 
+#include <type_traits>
+
 #include "pkv_device.h"
 #include "pkv_launch.h"
 
@@ -46,6 +48,10 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kTile = 32;                      // tokens per wave tile
 constexpr int kMaxRangePages = 512;            // block-table entries staged per work item
+// A head's running max moves only when a score exceeds it by more than this
+// (log2 units); the final (m, l, acc) describes the same softmax whichever
+// shift was used.
+constexpr float kSlack = 8.0f;
 
 typedef __bf16 bf16x8_t __attribute__((__vector_size__(16)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -70,14 +76,16 @@ struct TileRegs {
   u32x4 v[VLOADS];
 };
 
-// Page ids of the two 16-token blocks of the tile at t0 (a block past the end
-// reuses the first block's page: in bounds, and masked later).  `pages` holds
-// the block-table entries of this work item's range, from entry `first`.
+// Page ids of the two 16-token blocks of the tile at t0 < t_end.  A block
+// past the end looks up the page of token t_end - 1, which is block 0's page
+// (16-token blocks never straddle a page): in bounds, and masked later.
+// `pages` holds the block-table entries of this work item's range, from
+// entry `first`.
 __device__ __forceinline__ void tile_pages(const int32_t* pages,
                                            int first, int t0, int t_end,
                                            int pshift, int& p0, int& p1) {
   p0 = pages[(t0 >> pshift) - first];
-  p1 = (t0 + 16 < t_end) ? pages[((t0 + 16) >> pshift) - first] : p0;
+  p1 = pages[(min(t0 + 16, t_end - 1) >> pshift) - first];
 }
 
 // First of the 8 consecutive d values that MFMA step kk takes for lane group g:
@@ -89,34 +97,38 @@ __device__ __forceinline__ int k_elem_offset(int kk, int g) {
   else return 32 * kk + 8 * g;
 }
 
+// Loads of one tile.  The row of a block is the same for the whole wave (page
+// ids are wave-uniform), so the block's base addresses stay in scalar
+// registers and every lane adds only its fixed offset `loff` = byte offset of
+// its first piece in the block (row l/R, piece l%R); the load i of a block is
+// a further i*RPI rows.
 template <int KVT, int D>
 __device__ __forceinline__ void load_tile(TileRegs<KVT, D>& r, const uint8_t* kp, const uint8_t* vp,
                                           int p0, int p1, int t0, int t_end, int Hkv, int j,
-                                          int pshift, int lane) {
+                                          int pshift, uint32_t loff) {
   using TR = TileRegs<KVT, D>;
   constexpr int ROWB = TR::VROWB;
+  constexpr int R = ROWB / 16, RPI = 64 / R, LPB = TR::VLOADS / 2;
   const int pmask = (1 << pshift) - 1;
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
     const int tb = (blk == 1 && t0 + 16 >= t_end) ? t0 : t0 + 16 * blk;
     const int page = blk == 0 ? p0 : p1;
     const size_t row = (((size_t)page * Hkv + j) << pshift | (size_t)(tb & pmask));
-    // K and V: rows of this block, 16-byte pieces in row-major order
-    constexpr int R = ROWB / 16;                 // lanes per row
-    constexpr int RPI = 64 / R;                  // rows per load instruction
-    constexpr int LPB = TR::VLOADS / 2;          // loads per lane per block
+    const uint8_t* kb = kp + row * ROWB;
+    const uint8_t* vb = vp + row * ROWB;
 #pragma unroll
     for (int i = 0; i < LPB; ++i) {
-      const int rr = (lane / R) + RPI * i;       // row within the block (0..15)
-      const size_t off = (row + rr) * ROWB + (size_t)(lane % R) * 16;
-      r.k[blk * LPB + i] = ld16_stream(kp + off);
-      r.v[blk * LPB + i] = ld16_stream(vp + off);
+      r.k[blk * LPB + i] = ld16_stream(kb + loff + i * RPI * ROWB);
+      r.v[blk * LPB + i] = ld16_stream(vb + loff + i * RPI * ROWB);
     }
   }
 }
 
 template <int KVT, int D>
-__global__ __launch_bounds__(256, 2) void decode_partial_mfma(AttnArgs a) {
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(KvBytes<KVT>::value == 1 || D == 64 ? 3 : 2)))
+void decode_partial_mfma(AttnArgs a) {
   using TR = TileRegs<KVT, D>;
   constexpr int KK = D / 32;                    // MFMA steps over d
   constexpr int DT = D / 16;                    // 16-wide d tiles of the output
@@ -159,6 +171,35 @@ __global__ __launch_bounds__(256, 2) void decode_partial_mfma(AttnArgs a) {
   if constexpr (KvCoded<KVT>::value) { kscale = a.c.k_scale[j]; vscale = a.c.v_scale[j]; }
   const float smul = a.sm_scale * kLog2e * kscale;
 
+  const int32_t* btrow = a.bt + (size_t)z * a.bt_stride;
+  const uint8_t* kp = static_cast<const uint8_t*>(a.c.k_pool);
+  const uint8_t* vp = static_cast<const uint8_t*>(a.c.v_pool);
+  uint8_t* lds = smem + w * kTile * LDS_ROW;
+  constexpr int STRIDE = kWaves * kTile;
+  const uint32_t loff = (uint32_t)((lane / R) * ROWB + (lane % R) * 16);
+  // This wave's tiles are t_begin + w*kTile + k*STRIDE, k = 0..nt-1.
+  const int tw0 = t_begin + w * kTile;
+  const int nt = tw0 < t_end ? (t_end - tw0 + STRIDE - 1) / STRIDE : 0;
+
+  // Prologue, ordered so that its memory latencies overlap: the range's
+  // block-table entries (for the LDS copy below; at most 2 per thread, the
+  // host keeps ranges within kMaxRangePages pages), the page ids of this
+  // wave's first two tiles straight from the table, then Q, then the first
+  // tile's K/V loads, which wait only for their own two page ids.
+  const int first = t_begin >> pshift;
+  const int npg = ((t_end - 1) >> pshift) - first + 1;
+  // (Indices are clamped rather than branched on, so that no wait has to
+  // cover a branch: entries past the range repeat its last one, and the page
+  // ids of tiles this wave does not have are those of the range's last token.)
+  const int bte0 = btrow[first + min((int)threadIdx.x, npg - 1)];
+  const int bte1 = btrow[first + min((int)threadIdx.x + 256, npg - 1)];
+  // A wave without tiles (nt == 0) loads the range's last 16-aligned block
+  // instead and never uses it.
+  const int ta = tw0 < t_end ? tw0 : ((t_end - 1) & ~15);
+  int pn0, pn1, pq0, pq1;                       // pages of tiles 0 and 1 of this wave
+  tile_pages(btrow, 0, ta, t_end, pshift, pn0, pn1);
+  tile_pages(btrow, 0, min(tw0 + STRIDE, t_end - 1), t_end, pshift, pq0, pq1);
+
   // Q^T as B operand: lane (g, h) holds Q[j*G + h][d] for the d's that MFMA
   // step kk takes from K (k_elem_offset); zero for h >= G.
   u32x4 qb[KK];
@@ -169,47 +210,40 @@ __global__ __launch_bounds__(256, 2) void decode_partial_mfma(AttnArgs a) {
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) qb[kk] = ld16(q + k_elem_offset<KVT>(kk, g4));
   }
+
+  // Two register images alternate: while one tile is computed the next one's
+  // loads are in flight, and the page ids of the tile after that are read
+  // from LDS.  The main loop only runs while a next tile exists, so every
+  // load in it is unconditional and the wait for the current tile's data
+  // never has to cover the next tile's loads; the last tiles are peeled.
+  // Only a range's last tile can hold tokens past its end, so every tile of
+  // the main loop is computed without masks.
+  TR buf0, buf1;
+  load_tile<KVT, D>(buf0, kp, vp, pn0, pn1, ta, t_end, Hkv, j, pshift, loff);
+  pn0 = pq0;                                    // pages of the next tile to load
+  pn1 = pq1;
+
+  // The range's block-table entries, staged in LDS once: later page lookups
+  // then never wait behind the K/V loads in flight (vector-memory waits
+  // retire in order).
+  __shared__ int32_t pages[kMaxRangePages];
+  pages[threadIdx.x] = bte0;
+  pages[threadIdx.x + 256] = bte1;
+  __syncthreads();
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) settle(qb[kk]);
 
   f32x4 o[DT];
 #pragma unroll
   for (int i = 0; i < DT; ++i) o[i] = f32x4{0, 0, 0, 0};
+  // Running max m of head h (log2 domain; the same in the 4 lanes of h) and
+  // this lane's share l of the head's running sum (its 8 tokens per tile).
   float m = -INFINITY, l = 0.0f;
 
-  const int32_t* btrow = a.bt + (size_t)z * a.bt_stride;
-  // The range's block-table entries, staged in LDS once: page lookups then
-  // never wait behind the K/V loads in flight (vector-memory waits retire in
-  // order).  The host routes ranges of more than kMaxRangePages pages to the
-  // vector path.
-  __shared__ int32_t pages[kMaxRangePages];
-  const int first = t_begin >> pshift;
-  const int npg = ((t_end - 1) >> pshift) - first + 1;
-  for (int i = threadIdx.x; i < npg; i += blockDim.x) pages[i] = btrow[first + i];
-  __syncthreads();
-  const uint8_t* kp = static_cast<const uint8_t*>(a.c.k_pool);
-  const uint8_t* vp = static_cast<const uint8_t*>(a.c.v_pool);
-  uint8_t* lds = smem + w * kTile * LDS_ROW;
-  constexpr int STRIDE = kWaves * kTile;
-
-  // This wave's tiles are t_begin + w*kTile + k*STRIDE, k = 0..nt-1.  Two
-  // register images alternate: while one tile is computed the next one's
-  // loads are in flight, and the page ids of the tile after that are read
-  // from LDS.  The main loop only runs while a next tile exists, so every
-  // load in it is unconditional and the wait for the current tile's data
-  // never has to cover the next tile's loads; the last tiles are peeled.
-  const int tw0 = t_begin + w * kTile;
-  const int nt = tw0 < t_end ? (t_end - tw0 + STRIDE - 1) / STRIDE : 0;
-  TR buf0, buf1;
-  int pn0 = 0, pn1 = 0;                         // pages of the next tile to load
-  if (nt > 0) {
-    tile_pages(pages, first, tw0, t_end, pshift, pn0, pn1);
-    load_tile<KVT, D>(buf0, kp, vp, pn0, pn1, tw0, t_end, Hkv, j, pshift, lane);
-    if (nt > 1) tile_pages(pages, first, tw0 + STRIDE, t_end, pshift, pn0, pn1);
-  }
-
-  auto compute = [&](const TR& cur, const int t0) {
-    const bool full = t0 + kTile <= t_end;
+  // compute(cur, t0, FULL): tile t0 from the register image cur; FULL tiles
+  // have all 32 tokens inside the range.
+  auto compute = [&](const TR& cur, const int t0, auto full_c) {
+    constexpr bool FULL = decltype(full_c)::value;
 
     // ---- K rows -> LDS (raw storage format, padded rows) ----
 #pragma unroll
@@ -222,7 +256,7 @@ __global__ __launch_bounds__(256, 2) void decode_partial_mfma(AttnArgs a) {
 
     // ---- S^T = K Q^T for the two 16-token blocks ----
     // A operand of step kk, lane (g, n): token n, 16-byte piece 4*(kk / SPP) + g
-    // (SPP = MFMA steps per piece: 1 for bf16, 2 for fp8).
+    // (SPP = MFMA steps per piece: 1 for bf16, 2 for 8-bit codes).
     f32x4 s[2];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
@@ -254,16 +288,21 @@ __global__ __launch_bounds__(256, 2) void decode_partial_mfma(AttnArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int tok = 16 * blk + 4 * g4 + r;
-        sv[4 * blk + r] = (full || t0 + tok < t_end) ? s[blk][r] : -INFINITY;
+        sv[4 * blk + r] = (FULL || t0 + tok < t_end) ? s[blk][r] : -INFINITY;
       }
+    // Each lane checks its own 8 scores against the head's running max; only
+    // when some score exceeds it by more than kSlack (always on the first
+    // tile, rarely afterwards) does the wave reduce the max over each head's
+    // 4 lanes and rescale.  Until then p stays below 2^kSlack.  Every head
+    // has a valid token in every tile, so m is finite from the first tile on.
     float mx = sv[0];
 #pragma unroll
     for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mn = fmaxf(m, mx * smul);        // finite: every tile has a valid token
-    if (__any(mn > m)) {                         // rescale only when some head's max grew
-      const float alpha = __builtin_amdgcn_exp2f(m - mn);
+    if (__any(mx * smul > m + kSlack)) {
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mn = fmaxf(m, mx * smul);
+      const float alpha = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - mn);
       l *= alpha;
 #pragma unroll
       for (int i = 0; i < DT; ++i) o[i] *= alpha;
@@ -289,7 +328,7 @@ __global__ __launch_bounds__(256, 2) void decode_partial_mfma(AttnArgs a) {
         const int rr = (lane / R) + RPI * i;
         const int tok = 16 * blk + rr;
         u32x4 x = cur.v[blk * LPB + i];
-        if (!full && t0 + tok >= t_end) x = u32x4{0, 0, 0, 0};
+        if (!FULL && t0 + tok >= t_end) x = u32x4{0, 0, 0, 0};
         if constexpr (KvCoded<KVT>::value) {
           u32x4 lo, hi;
           code16_to_bf16<KVT>(x, lo, hi);
@@ -321,14 +360,17 @@ __global__ __launch_bounds__(256, 2) void decode_partial_mfma(AttnArgs a) {
       o[dt] = mfma16(va, pb, o[dt]);
     }
   };
+  const std::integral_constant<bool, true> kFull;
+  const std::integral_constant<bool, false> kPartial;
   // step(k, cur, nxt): load tile k+1 into nxt (its pages are pn0/pn1), read
-  // the pages of tile k+2, compute tile k from cur.
+  // the pages of tile k+2, compute tile k (never the range's last) from cur.
   auto step = [&](int k, const TR& cur, TR& nxt) {
     const int tn = tw0 + (k + 1) * STRIDE;
-    load_tile<KVT, D>(nxt, kp, vp, pn0, pn1, tn, t_end, Hkv, j, pshift, lane);
+    load_tile<KVT, D>(nxt, kp, vp, pn0, pn1, tn, t_end, Hkv, j, pshift, loff);
     if (k + 2 < nt) tile_pages(pages, first, tn + STRIDE, t_end, pshift, pn0, pn1);
-    compute(cur, tw0 + k * STRIDE);
+    compute(cur, tw0 + k * STRIDE, kFull);
   };
+  auto last = [&](const TR& cur, const int t0) { compute(cur, t0, kPartial); };
   int k = 0;
   for (; k + 2 < nt; k += 2) {
     step(k, buf0, buf1);
@@ -336,9 +378,9 @@ __global__ __launch_bounds__(256, 2) void decode_partial_mfma(AttnArgs a) {
   }
   if (k + 1 < nt) {                              // two tiles left: buf0 holds tile k
     step(k, buf0, buf1);
-    compute(buf1, tw0 + (k + 1) * STRIDE);
+    last(buf1, tw0 + (k + 1) * STRIDE);
   } else if (k < nt) {                           // one tile left
-    compute(buf0, tw0 + k * STRIDE);
+    last(buf0, tw0 + k * STRIDE);
   }
 
   // ---- merge: 4 lanes per head within the wave (l is lane-partial) ----
