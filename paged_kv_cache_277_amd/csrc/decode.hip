@@ -194,39 +194,35 @@ __global__ __launch_bounds__(256) void decode_partial_vec(AttnArgs a) {
   };
   constexpr int STRIDE = kWaves * TOK;
 
-  // Software pipeline: the next tile's K/V loads are in flight while the
-  // current tile is scored; block-table entries are read one tile ahead.
-  int t0 = t_begin + w * TOK;
-  u32x4 kA[U], vA[U];
-  int page_next = 0;
-  if (t0 < t_end) {
-    const size_t base = tile_base(btrow[t0 >> pshift], t0);
+  // Software pipeline.  This wave's tiles start at tw0 + k*STRIDE, k < nt.
+  // Two register images alternate: while one tile is scored the next one's
+  // K/V loads are in flight.  Page ids are read from the block table two
+  // tiles ahead, each before the K/V loads of the tile after the current one,
+  // so that every wait (vector loads retire in order) covers only what the
+  // next step needs.  The main loop runs only while two more tiles exist, so
+  // its loads are unconditional (page lookups past the range are clamped to
+  // its last token) and no wait has to cover a branch; the last tiles are
+  // peeled.
+  const int tw0 = t_begin + w * TOK;
+  const int nt = tw0 < t_end ? (t_end - tw0 + STRIDE - 1) / STRIDE : 0;
+  auto page_of = [&](int k) { return btrow[min(tw0 + k * STRIDE, t_end - 1) >> pshift]; };
+  auto load = [&](u32x4 (&kd)[U], u32x4 (&vd)[U], int page, int t) {
+    const size_t base = tile_base(page, t);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      kA[u] = ld16_stream(kp + base + (size_t)u * RW * ROWB);
-      vA[u] = ld16_stream(vp + base + (size_t)u * RW * ROWB);
+      kd[u] = ld16_stream(kp + base + (size_t)u * RW * ROWB);
+      vd[u] = ld16_stream(vp + base + (size_t)u * RW * ROWB);
     }
-    if (t0 + STRIDE < t_end) page_next = btrow[(t0 + STRIDE) >> pshift];
-  }
-  for (; t0 < t_end; t0 += STRIDE) {
-    const int t1 = t0 + STRIDE;
-    u32x4 kB[U], vB[U];
-    if (t1 < t_end) {
-      const size_t base = tile_base(page_next, t1);
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        kB[u] = ld16_stream(kp + base + (size_t)u * RW * ROWB);
-        vB[u] = ld16_stream(vp + base + (size_t)u * RW * ROWB);
-      }
-      if (t1 + STRIDE < t_end) page_next = btrow[(t1 + STRIDE) >> pshift];
-    }
+  };
+  auto compute = [&](const u32x4 (&kc)[U], const u32x4 (&vc_in)[U], const int t0) {
     const bool full = t0 + TOK <= t_end;
+    u32x4 vc[U];
     float sc[GMAX][U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const bool valid = full || (t0 + u * RW + rg < t_end);
       float kf[EPL];
-      piece_to_f32<KVT>(kA[u], kf);
+      piece_to_f32<KVT>(kc[u], kf);
 #pragma unroll
       for (int g = 0; g < GMAX; ++g) {
         float s = 0.0f;
@@ -237,7 +233,7 @@ __global__ __launch_bounds__(256) void decode_partial_vec(AttnArgs a) {
         s = group_sum<R>(s);
         sc[g][u] = valid ? s : -INFINITY;
       }
-      if (!valid) vA[u] = u32x4{0, 0, 0, 0};   // unused slots may hold NaN
+      vc[u] = valid ? vc_in[u] : u32x4{0, 0, 0, 0};   // rows past the end may hold NaN
     }
     float p[GMAX][U];
 #pragma unroll
@@ -262,7 +258,7 @@ __global__ __launch_bounds__(256) void decode_partial_vec(AttnArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float vf[EPL];
-      piece_to_f32<KVT>(vA[u], vf);
+      piece_to_f32<KVT>(vc[u], vf);
 #pragma unroll
       for (int g = 0; g < GMAX; ++g) {
         if (g < G) {
@@ -271,8 +267,33 @@ __global__ __launch_bounds__(256) void decode_partial_vec(AttnArgs a) {
         }
       }
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u) { kA[u] = kB[u]; vA[u] = vB[u]; }
+  };
+
+  // Prologue: a wave without tiles (nt == 0) loads the range's last tile
+  // instead and never uses it (in bounds, and no branch around the loads).
+  u32x4 kA[U], vA[U], kB[U], vB[U];
+  const int ta = tw0 < t_end ? tw0 : ((t_end - 1) & ~(TOK - 1));
+  const int pg0 = btrow[ta >> pshift];
+  int pg_next = page_of(1);
+  load(kA, vA, pg0, ta);
+  // step(k): page id of tile k+2, loads of tile k+1 into nxt, score tile k.
+  auto step = [&](int k, const u32x4 (&kc)[U], const u32x4 (&vc)[U], u32x4 (&kn)[U],
+                  u32x4 (&vn)[U]) {
+    const int pg = pg_next;
+    pg_next = page_of(k + 2);
+    load(kn, vn, pg, tw0 + (k + 1) * STRIDE);
+    compute(kc, vc, tw0 + k * STRIDE);
+  };
+  int k = 0;
+  for (; k + 2 < nt; k += 2) {
+    step(k, kA, vA, kB, vB);
+    step(k + 1, kB, vB, kA, vA);
+  }
+  if (k + 1 < nt) {                              // two tiles left: A holds tile k
+    step(k, kA, vA, kB, vB);
+    compute(kB, vB, tw0 + (k + 1) * STRIDE);
+  } else if (k < nt) {                           // one tile left
+    compute(kA, vA, tw0 + k * STRIDE);
   }
 
   // Merge the row-groups of this wave (lanes that share `col`).
