@@ -103,18 +103,21 @@ int32_t default_split(const pkv_cache_desc* c, int32_t num_seqs, int32_t num_q_h
   const int G = num_q_heads / c->num_kv_heads;
   int split;
   if (G >= 3 && c->kv_dtype != PKV_F32) {
-    // Matrix-core path (2 waves/SIMD): long ranges amortise each work
-    // item's start-up, but the grid must keep ~2048 items.  With only the
-    // longest context known, the expected item count assumes contexts
-    // average half of it.  Ranges of 512..2048 tokens.
+    // Matrix-core path: long ranges amortise each work item's start-up,
+    // but the grid must keep ~2048 items.  With only the longest context
+    // known, the expected item count assumes contexts average half of it.
+    // Ranges of 512 tokens up to 1 MiB of K+V per KV head (2048 tokens of
+    // 16-bit, 4096 of 8-bit codes at head_dim 128).
+    const bool coded = c->kv_dtype == PKV_FP8_E4M3FN || c->kv_dtype == PKV_INT8;
+    const int cap = coded ? 4096 : 2048;
     split = 512;
-    while (split < 2048 && pairs * ceil_div(std::max(1, max_len), 2 * split) / 2 >= 2048) split *= 2;
+    while (split < cap && pairs * ceil_div(std::max(1, max_len), 2 * split) / 2 >= 2048) split *= 2;
   } else {
-    // Vector path: ~256 KiB of K+V per KV head and item (512 tokens of
-    // 16-bit or 1024 of fp8 at head_dim 128); shorter ranges when the batch
-    // would give fewer than ~8 items per CU, never below 256 tokens (the merge
-    // would cost more than the parallelism gains).
-    split = (c->kv_dtype == PKV_FP8_E4M3FN || c->kv_dtype == PKV_INT8) ? 1024 : 512;
+    // Vector path: ~512 KiB of K+V per KV head and item (1024 tokens of
+    // 16-bit or 2048 of 8-bit codes at head_dim 128); shorter ranges when the
+    // batch would give fewer than ~8 items per CU, never below 256 tokens (the
+    // merge would cost more than the parallelism gains).
+    split = (c->kv_dtype == PKV_FP8_E4M3FN || c->kv_dtype == PKV_INT8) ? 2048 : 1024;
     if (c->head_dim == 64) split *= 2;
     const int floor_split = 256;
     while (split / 2 >= floor_split && pairs * ceil_div(std::max(1, max_len), split) < 8 * kNumCUs)
