@@ -113,11 +113,12 @@ int32_t default_split(const pkv_cache_desc* c, int32_t num_seqs, int32_t num_q_h
     split = 512;
     while (split < cap && pairs * ceil_div(std::max(1, max_len), 2 * split) / 2 >= 2048) split *= 2;
   } else {
-    // Vector path: ~512 KiB of K+V per KV head and item (1024 tokens of
-    // 16-bit or 2048 of 8-bit codes at head_dim 128); shorter ranges when the
-    // batch would give fewer than ~8 items per CU, never below 256 tokens (the
-    // merge would cost more than the parallelism gains).
-    split = (c->kv_dtype == PKV_FP8_E4M3FN || c->kv_dtype == PKV_INT8) ? 2048 : 1024;
+    // Vector path: 1024 tokens per KV head and item (512 KiB of 16-bit K+V
+    // at head_dim 128; 8-bit codes measured no better with longer ranges);
+    // shorter ranges when the batch would give fewer than ~8 items per CU,
+    // never below 256 tokens (the merge would cost more than the parallelism
+    // gains).
+    split = 1024;
     if (c->head_dim == 64) split *= 2;
     const int floor_split = 256;
     while (split / 2 >= floor_split && pairs * ceil_div(std::max(1, max_len), split) < 8 * kNumCUs)
