@@ -13,11 +13,13 @@
 // Lane layouts of the 16x16x32 bf16 MFMA (wave64): A[i][k] in lane i%16 +
 // 16*(k/8), element k%8; B[k][j] in lane j + 16*(k/8); C[i][j] in lane
 // j + 16*(i/4), element i%4.  Consequences used below:
-//   * K rows go straight from HBM to the A operand: lane l holds token l%16;
-//     its load i reads 16-byte piece 4i + g (g = l/16) of the row, so each load
-//     instruction reads 64 contiguous bytes of 16 rows.  For bf16, step kk
-//     uses d = 32kk + 8g + e; for fp8 (16 codes per piece) d = 64(kk/2) + 16g +
-//     8(kk%2) + e.  Q^T (B operand) is loaded in the same d order.
+//   * K and V rows are loaded whole (each load instruction reads contiguous
+//     row bytes, with the streaming hint) and K is written, in its storage
+//     format, to the wave's padded LDS slice.  The A operand of step kk is
+//     read back per lane: token l%16, 16-byte piece 4*(kk/SPP) + g (g = l/16,
+//     SPP = MFMA steps per piece).  For bf16, step kk uses d = 32kk + 8g + e;
+//     for 8-bit codes (16 per piece, widened in registers) d = 64(kk/2) + 16g
+//     + 8(kk%2) + e.  Q^T (B operand) is loaded in the same d order.
 //   * The S^T result leaves, in lane l, head h = l%16 for tokens 4g+r of each
 //     16-token block; over the two blocks of a tile that is 8 tokens of one
 //     head — exactly a B operand row of P^T if the tile's tokens are taken in
