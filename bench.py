@@ -61,46 +61,62 @@ def measured_traffic(spec_name: str):
         return None
 
 
-def cpu_baseline(wl, budget_s: float = 12.0) -> dict:
+def cpu_baseline(wl, budget_s: float = 12.0, budget_1thread_s: float = 4.0) -> dict:
     """The oracle, as it stands, on the sequences of the workload in order
     (repeating the pass if it is short) until about `budget_s` seconds of
     decode work; scaled to GB/s of the same algorithmic bytes per sequence
-    the GPU figure uses."""
+    the GPU figure uses.  A second, shorter run with the BLAS pools limited to
+    one thread gives the single-core figure."""
     from oracle import attention as oa
     from paged_kv_cache_277_amd import workloads as wk
 
     s = wl.spec
-    done, bytes_done, t_total, tokens = 0, 0, 0.0, 0
     kp, vp = wl.poisoned_pool()
     filled = set()
-    passes = 0
-    while t_total < budget_s and passes < 50:
-        passes += 1
-        for b in range(wl.num_seqs):
-            if b not in filled:
-                owners = {("seq", b)}
-                rows_s = [i for i, o in enumerate(wl.setup.owners) if o in owners or o[0] == "prefix"]
-                rows_t = [i for i, o in enumerate(wl.step.owners) if o in owners or o[0] == "prefix"]
-                for batch, rows in ((wl.setup, rows_s), (wl.step, rows_t)):
-                    oa.kv_cache_append(kp, vp, s.kv_dtype, batch.k, batch.v, s.kv_in_dtype,
-                                       batch.cu, batch.start_pos, batch.block_tables, wl.k_scale,
-                                       wl.v_scale, rows=rows)
-                filled.add(b)
-            t0 = time.perf_counter()
-            oa.paged_attn_decode(wl.q, s.q_dtype, kp, vp, s.kv_dtype, wl.block_tables,
-                                 wl.context_lens, wl.sm_scale, wl.k_scale, wl.v_scale,
-                                 seqs=np.array([b]))
-            t_total += time.perf_counter() - t0
-            done += 1
-            tokens += int(wl.context_lens[b])
-            bytes_done += wk.decode_bytes(s, wl.context_lens[[b]], unique_prefix=False)
-            if t_total >= budget_s:
-                break
-    return {"value": round(bytes_done / t_total / 1e9, 4), "unit": "GB/s", "cores": _threads_used(),
-            "kind": "oracle",
-            "sample": f"fp64 oracle decode of {done} sequence-queries ({passes} pass(es) over the "
-                      f"{wl.num_seqs} sequences in order, {tokens} context tokens) in "
-                      f"{t_total:.1f} s"}
+
+    def run(budget):
+        done, bytes_done, t_total, tokens, passes = 0, 0, 0.0, 0, 0
+        while t_total < budget and passes < 50:
+            passes += 1
+            for b in range(wl.num_seqs):
+                if b not in filled:
+                    owners = {("seq", b)}
+                    rows_s = [i for i, o in enumerate(wl.setup.owners)
+                              if o in owners or o[0] == "prefix"]
+                    rows_t = [i for i, o in enumerate(wl.step.owners)
+                              if o in owners or o[0] == "prefix"]
+                    for batch, rows in ((wl.setup, rows_s), (wl.step, rows_t)):
+                        oa.kv_cache_append(kp, vp, s.kv_dtype, batch.k, batch.v, s.kv_in_dtype,
+                                           batch.cu, batch.start_pos, batch.block_tables,
+                                           wl.k_scale, wl.v_scale, rows=rows)
+                    filled.add(b)
+                t0 = time.perf_counter()
+                oa.paged_attn_decode(wl.q, s.q_dtype, kp, vp, s.kv_dtype, wl.block_tables,
+                                     wl.context_lens, wl.sm_scale, wl.k_scale, wl.v_scale,
+                                     seqs=np.array([b]))
+                t_total += time.perf_counter() - t0
+                done += 1
+                tokens += int(wl.context_lens[b])
+                bytes_done += wk.decode_bytes(s, wl.context_lens[[b]], unique_prefix=False)
+                if t_total >= budget:
+                    break
+        return bytes_done / t_total / 1e9, done, passes, tokens, t_total
+
+    gbs, done, passes, tokens, t_total = run(budget_s)
+    out = {"value": round(gbs, 4), "unit": "GB/s", "cores": _threads_used(), "kind": "oracle",
+           "sample": f"fp64 oracle decode of {done} sequence-queries ({passes} pass(es) over the "
+                     f"{wl.num_seqs} sequences in order, {tokens} context tokens) in "
+                     f"{t_total:.1f} s"}
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:
+        return out
+    with threadpool_limits(limits=1):
+        gbs1, done1, _, tokens1, t1 = run(budget_1thread_s)
+    out["value_1thread"] = round(gbs1, 4)
+    out["sample_1thread"] = (f"the same, BLAS limited to one thread: {done1} sequence-queries "
+                             f"({tokens1} context tokens) in {t1:.1f} s")
+    return out
 
 
 def copy_calibration(args) -> int:
