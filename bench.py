@@ -223,7 +223,10 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps first (default: 200 for a step with a prefill part, "
+                         "whose matrix-core kernel reaches steady clocks only after ~20 ms of "
+                         "work; 10 otherwise)")
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--kv-format", choices=("fp8", "int8"), default=None,
@@ -255,6 +258,8 @@ def main() -> int:
     from paged_kv_cache_277_amd import workloads as wk
 
     torch.cuda.set_device(0)
+    if args.warmup is None and (args.copy_calibration or args.chunk_sweep):
+        args.warmup = 2
     if args.copy_calibration:
         return copy_calibration(args)
     if args.chunk_sweep:
@@ -265,6 +270,8 @@ def main() -> int:
     wl = wk.make_workload(spec)
     print(f"[bench] workload {spec.name}: generated in {time.perf_counter() - t0:.1f} s",
           file=sys.stderr, flush=True)
+    if args.warmup is None:
+        args.warmup = 200 if wl.pf_block_tables is not None else 10
     dw = dev.upload(wl, "cuda", split_tokens=args.split_tokens)
     dw.setup()
     torch.cuda.synchronize()
