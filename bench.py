@@ -258,8 +258,10 @@ def main() -> int:
     from paged_kv_cache_277_amd import workloads as wk
 
     torch.cuda.set_device(0)
-    if args.warmup is None and (args.copy_calibration or args.chunk_sweep):
+    if args.warmup is None and args.copy_calibration:
         args.warmup = 2
+    if args.warmup is None and args.chunk_sweep:
+        args.warmup = 10            # matrix-core work: steady clocks after ~20 ms
     if args.copy_calibration:
         return copy_calibration(args)
     if args.chunk_sweep:
