@@ -191,7 +191,8 @@ pkv_status pkv_kv_cache_append(const pkv_cache_desc* cache,
  *                page_size; 0 selects pkv_decode_split_tokens().
  * workspace    : device scratch of at least pkv_decode_workspace_bytes(...)
  *                bytes (may be NULL when that size is 0); contents on entry
- *                are ignored.
+ *                are ignored.  It holds the partials and, for
+ *                pkv_mixed_step, the decode work list.
  * ------------------------------------------------------------------------ */
 
 /* Default split length for a decode batch: a multiple of page_size chosen
@@ -341,6 +342,15 @@ size_t pkv_context_fmha_workspace_bytes(int32_t num_seqs, int32_t num_tokens,
  * join are stream events, so a graph captured from `stream` records all of
  * it.  Both streams belong to the current device.  With side_stream NULL the
  * parts run one after another on `stream`.
+ *
+ * Decode work list: when the step has an append part and the decode does
+ * not run beside a prefill, a decode of at least 1024 (sequence, context
+ * range, KV head) work items takes its (sequence, range) items longest
+ * first, so that the launch ends on its shortest items; one extra workgroup
+ * of the append launch sorts them by token count (it reads only
+ * context_lens).  The list lives in the decode workspace
+ * (pkv_decode_workspace_bytes counts it).  Results are bit for bit those of
+ * pkv_paged_attn_decode with the same arguments.
  *
  * Every part is checked on the host before anything is launched.  When the
  * two attention parts run concurrently their workspaces must not overlap

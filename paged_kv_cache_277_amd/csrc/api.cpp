@@ -146,11 +146,21 @@ size_t workspace_bytes(const pkv_cache_desc* c, int32_t num_seqs, int32_t num_q_
                        int32_t max_len, int32_t split) {
   const int32_t ms = ceil_div(std::max(0, max_len), split);
   if (ms <= 1 || num_seqs <= 0) return 0;
-  // acc [rows][Hq][ms][D] + (m, l) [rows][Hq][ms][2], float32, each 256-byte aligned
+  // acc [rows][Hq][ms][D] + (m, l) [rows][Hq][ms][2], float32, + the work
+  // list {count, 0, (row, range) x rows*ms}, int32; each 256-byte aligned
   const size_t n = (size_t)num_seqs * num_q_heads * ms;
   const size_t acc = (n * c->head_dim * 4 + 255) / 256 * 256;
   const size_t ml = (n * 2 * 4 + 255) / 256 * 256;
-  return acc + ml;
+  const size_t list = ((2 + 2 * (size_t)num_seqs * ms) * 4 + 255) / 256 * 256;
+  return acc + ml + list;
+}
+
+// The work-list area of a decode workspace laid out by workspace_bytes.
+int32_t* decode_list_area(const pkv::AttnArgs& a) {
+  const size_t n = (size_t)a.num_rows * a.num_q_heads * a.max_splits;
+  const size_t acc = (n * a.c.head_dim * 4 + 255) / 256 * 256;
+  const size_t ml = (n * 2 * 4 + 255) / 256 * 256;
+  return reinterpret_cast<int32_t*>(reinterpret_cast<char*>(a.ws_acc) + acc + ml);
 }
 
 struct DecodeSetup {
@@ -637,8 +647,20 @@ pkv_status pkv_mixed_step(const pkv_cache_desc* cache, const pkv_append_batch* a
     return fail(PKV_ERR_INVALID_ARG, "decode and prefill workspaces overlap (they run concurrently)");
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipStream_t side = static_cast<hipStream_t>(side_stream);
-  if (ap && (st = hip_status(pkv::launch_append(aa, s), "mixed_step: append")) != PKV_OK) return st;
   const bool fork = dp && pp && side && side != s;
+  // A decode with enough work items that has the GPU to itself gets a work
+  // list (longest ranges first), written by one extra workgroup of the
+  // append launch, which precedes the decode on `stream`: no further launch
+  // and no cross-stream wait.  Beside a concurrent prefill the plain grid
+  // order is kept: its long items first would take slots from the prefill,
+  // the step's longer branch (measured 148 against 135 us on the 8B mixed
+  // step).
+  if (ap && dp && !fork && da.ws_acc && pkv::decode_plan_useful(da)) {
+    da.plan = decode_list_area(da);
+    aa.list = pkv::DecodeListArgs{dp->context_lens, da.num_rows, da.split_tokens, da.max_splits,
+                                  da.plan};
+  }
+  if (ap && (st = hip_status(pkv::launch_append(aa, s), "mixed_step: append")) != PKV_OK) return st;
   if (!fork) {
     if (pp && (st = launch_prefill_call(pa, s)) != PKV_OK) return st;
     if (dp && (st = launch_decode_call(da, s)) != PKV_OK) return st;

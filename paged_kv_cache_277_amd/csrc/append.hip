@@ -10,6 +10,7 @@
 // Launch: one workgroup per new token; its threads cover the token's
 // Hkv x head_dim row in 16-byte output pieces, so every page row is written
 // with full 16-byte stores and the packed input is read contiguously.
+#include "decode_list.h"
 #include "pkv_device.h"
 #include "pkv_launch.h"
 
@@ -20,6 +21,10 @@ template <int KVT>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   constexpr int KVB = KvBytes<KVT>::value;
   constexpr int EPL = 16 / KVB;                  // cache elements per 16-byte piece
+  if (a.list.list && blockIdx.x == a.num_tokens) {   // the extra workgroup: decode work list
+    build_decode_list(a.list);
+    return;
+  }
   const int t = blockIdx.x;
   const int r = owner_row(a.cu, a.num_rows, t);
   const int pos = a.start_pos[r] + (t - a.cu[r]);
@@ -83,8 +88,9 @@ __global__ __launch_bounds__(256) void fp8_to_f32_kernel(const uint8_t* codes, f
 }  // namespace
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
-  if (a.num_tokens == 0) return hipSuccess;
-  const dim3 grid(a.num_tokens), block(a.c.num_kv_heads * a.c.head_dim >= 2048 ? 256 : 128);
+  if (a.num_tokens == 0 && !a.list.list) return hipSuccess;
+  const dim3 grid(a.num_tokens + (a.list.list ? 1 : 0));
+  const dim3 block(a.c.num_kv_heads * a.c.head_dim >= 2048 ? 256 : 128);
   switch (a.c.kv_dtype) {
     case KV_F32: hipLaunchKernelGGL(append_kernel<KV_F32>, grid, block, 0, s, a); break;
     case KV_BF16: hipLaunchKernelGGL(append_kernel<KV_BF16>, grid, block, 0, s, a); break;

@@ -25,6 +25,8 @@
 // m is kept in the log2 domain (scores are pre-multiplied by log2(e)).
 #include <math.h>
 
+#include <algorithm>
+
 #include <type_traits>
 
 #include "pkv_device.h"
@@ -133,7 +135,17 @@ __global__ __launch_bounds__(256) void decode_partial_vec(AttnArgs a) {
   // The slowest dimension counts ranges back from each row's last: the last
   // (partial, on average half-size) range of every row is dispatched last,
   // so the launch ends on short work items instead of full ones.
-  const int j = blockIdx.x, z = blockIdx.y;
+  // With a work list (decode only) blockIdx.y + gridDim.y * blockIdx.z
+  // indexes it instead (longest ranges first); workgroups past its end have
+  // nothing to do.
+  const int j = blockIdx.x;
+  int z = blockIdx.y, item_range = 0;
+  if (a.plan) {
+    const int idx = blockIdx.y + gridDim.y * blockIdx.z;
+    if (idx >= a.plan[0]) return;
+    z = a.plan[2 + 2 * idx];
+    item_range = a.plan[3 + 2 * idx];
+  }
   int L, btr;
   size_t qrow;
   if (!resolve_row(a, z, L, btr, qrow)) return;
@@ -141,7 +153,7 @@ __global__ __launch_bounds__(256) void decode_partial_vec(AttnArgs a) {
   const int pshift = a.page_shift, pmask = (1 << pshift) - 1;
   const int G = Hq / Hkv;
   if (L <= 0) {
-    if (blockIdx.z == a.max_splits - 1) {  // empty context: output 0, lse = -inf
+    if (a.plan || blockIdx.z == a.max_splits - 1) {  // empty context: output 0, lse = -inf
       for (int i = threadIdx.x; i < G * D; i += blockDim.x)
         store_o<QT>(a.out, (qrow * Hq + (size_t)j * G) * D + i, 0.0f);
       if (a.lse && threadIdx.x < G) a.lse[qrow * Hq + (size_t)j * G + threadIdx.x] = -INFINITY;
@@ -151,7 +163,7 @@ __global__ __launch_bounds__(256) void decode_partial_vec(AttnArgs a) {
   // (a length beyond max_splits ranges breaks the call's precondition: the
   // clamp keeps every write inside the workspace)
   const int n_split = min((L + a.split_tokens - 1) / a.split_tokens, a.max_splits);
-  const int split = n_split - a.max_splits + (int)blockIdx.z;
+  const int split = a.plan ? item_range : n_split - a.max_splits + (int)blockIdx.z;
   if (split < 0) return;
   const int t_begin = split * a.split_tokens;
   const int t_end = min(L, t_begin + a.split_tokens);
@@ -458,10 +470,23 @@ hipError_t launch_vec_any(const AttnArgs& a, dim3 grid, hipStream_t s) {
 
 }  // namespace
 
+// A work list is worth building when the call has enough workgroups for
+// their order to matter.
+bool decode_plan_useful(const AttnArgs& a) {
+  return !a.prefill && a.max_splits > 1 && a.num_rows > 0 &&
+         (int64_t)a.num_rows * a.max_splits * a.c.num_kv_heads >= 1024;
+}
+
+dim3 decode_plan_grid(const AttnArgs& a) {
+  const int64_t n = (int64_t)a.num_rows * a.max_splits;
+  const int y = (int)std::min<int64_t>(n, 65535);
+  return dim3(a.c.num_kv_heads, y, (unsigned)((n + y - 1) / y));
+}
+
 hipError_t launch_decode_partial(const AttnArgs& a, hipStream_t s) {
   if (a.num_rows == 0) return hipSuccess;
   if (decode_mfma_supported(a)) return launch_decode_partial_mfma(a, s);
-  const dim3 grid(a.c.num_kv_heads, a.num_rows, a.max_splits);
+  const dim3 grid = a.plan ? decode_plan_grid(a) : dim3(a.c.num_kv_heads, a.num_rows, a.max_splits);
   return launch_vec_any(a, grid, s);
 }
 

@@ -146,13 +146,22 @@ void decode_partial_mfma(AttnArgs a) {
 
   // Grid (KV head, row, range counted back from the row's last): the last,
   // partial range of every row is dispatched last (see decode.hip).
-  const int j = blockIdx.x, z = blockIdx.y;
+  // With a work list, blockIdx.y + gridDim.y * blockIdx.z indexes it instead
+  // (longest ranges first); workgroups past its end have nothing to do.
+  const int j = blockIdx.x;
+  int z = blockIdx.y, item_range = 0;
+  if (a.plan) {
+    const int idx = blockIdx.y + gridDim.y * blockIdx.z;
+    if (idx >= a.plan[0]) return;
+    z = a.plan[2 + 2 * idx];
+    item_range = a.plan[3 + 2 * idx];
+  }
   const int L = a.context_lens[z];
   const int Hq = a.num_q_heads, Hkv = a.c.num_kv_heads;
   const int G = Hq / Hkv;
   const size_t qrow = (size_t)z;
   if (L <= 0) {
-    if (blockIdx.z == a.max_splits - 1) {  // empty context: output 0, lse = -inf
+    if (a.plan || blockIdx.z == a.max_splits - 1) {  // empty context: output 0, lse = -inf
       for (int i = threadIdx.x; i < G * D; i += blockDim.x)
         static_cast<uint16_t*>(a.out)[(qrow * Hq + (size_t)j * G) * D + i] = 0;
       if (a.lse && threadIdx.x < G) a.lse[qrow * Hq + (size_t)j * G + threadIdx.x] = -INFINITY;
@@ -160,7 +169,7 @@ void decode_partial_mfma(AttnArgs a) {
     return;
   }
   const int n_split = min((L + a.split_tokens - 1) / a.split_tokens, a.max_splits);
-  const int split = n_split - a.max_splits + (int)blockIdx.z;
+  const int split = a.plan ? item_range : n_split - a.max_splits + (int)blockIdx.z;
   if (split < 0) return;
   const int t_begin = split * a.split_tokens;
   const int t_end = min(L, t_begin + a.split_tokens);
@@ -434,7 +443,8 @@ bool decode_mfma_supported(const AttnArgs& a) {
 }
 
 hipError_t launch_decode_partial_mfma(const AttnArgs& a, hipStream_t s) {
-  const dim3 grid(a.c.num_kv_heads, a.num_rows, a.max_splits), block(256);
+  const dim3 grid = a.plan ? decode_plan_grid(a) : dim3(a.c.num_kv_heads, a.num_rows, a.max_splits);
+  const dim3 block(256);
   if (a.c.kv_dtype == KV_BF16) {
     if (a.c.head_dim == 128) hipLaunchKernelGGL((decode_partial_mfma<KV_BF16, 128>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((decode_partial_mfma<KV_BF16, 64>), grid, block, 0, s, a);

@@ -17,6 +17,14 @@ struct CacheView {
   int32_t num_pages, num_kv_heads, page_size, head_dim, kv_dtype;
 };
 
+// Inputs of a decode work list (see decode_list.h): built by one extra
+// workgroup of the append launch that precedes the decode in a mixed step.
+struct DecodeListArgs {
+  const int32_t* context_lens;
+  int32_t num_rows, split_tokens, max_splits;
+  int32_t* list;                 // {count, 0, (row, range) x count}; null: no list
+};
+
 struct AppendArgs {
   CacheView c;
   const void* k_new;
@@ -26,6 +34,7 @@ struct AppendArgs {
   const int32_t* start_pos;
   const int32_t* bt;
   int32_t bt_stride, num_rows, num_tokens;
+  DecodeListArgs list;           // list.list null unless a decode list is wanted
 };
 
 // Rows of an attention launch are either decode sequences (one query each)
@@ -49,6 +58,9 @@ struct AttnArgs {
   float sm_scale;
   float* ws_acc;                 // [rows][Hq][max_splits][D]   (prefill rows: tokens)
   float* ws_ml;                  // [rows][Hq][max_splits][2]
+  // decode: work list {count, 0, (row, range) x count}, longest ranges
+  // first (decode_list.h); null: the grid walks (row, range) itself
+  int32_t* plan;
   int32_t prefill;
   int32_t contiguous;            // prefill over contiguous K/V [tokens][Hkv][D] (no pages)
   int32_t page_shift;            // log2(page_size)
@@ -57,6 +69,10 @@ struct AttnArgs {
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 hipError_t launch_decode_partial(const AttnArgs& a, hipStream_t s);
 hipError_t launch_lse_merge(const AttnArgs& a, hipStream_t s);
+// Decode work list: whether a call is worth one, and the grid of a decode
+// launch that reads it, (KV heads, y, z) with y * z >= rows * max_splits.
+bool decode_plan_useful(const AttnArgs& a);
+dim3 decode_plan_grid(const AttnArgs& a);
 hipError_t launch_prefill(const AttnArgs& a, hipStream_t s);
 // Grouped-query decode on the matrix cores (G >= 3, bf16 or fp8 KV).
 bool decode_mfma_supported(const AttnArgs& a);

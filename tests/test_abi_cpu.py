@@ -166,8 +166,9 @@ def test_workspace_and_split_planning():
     split = lib.pkv_decode_split_tokens(C.byref(d), 64, 40, 4096)
     assert split > 0 and split % 64 == 0
     ws = lib.pkv_decode_workspace_bytes(C.byref(d), 64, 40, 4096, 0)
-    n = 64 * 40 * (-(-4096 // split))
-    assert ws >= n * 128 * 4 + n * 8
+    ms = -(-4096 // split)
+    n = 64 * 40 * ms
+    assert ws >= n * 128 * 4 + n * 8 + (2 + 2 * 64 * ms) * 4     # partials + work list
     # one range covers everything -> no workspace
     assert lib.pkv_decode_workspace_bytes(C.byref(d), 64, 40, 64, 0) == 0
     assert lib.pkv_decode_workspace_bytes(C.byref(d), 64, 40, 4096, 4096) == 0

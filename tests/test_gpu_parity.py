@@ -379,6 +379,79 @@ def test_mixed_step_full_size():
     assert torch.isfinite(dw.pf["out"].float()).all()
 
 
+# Mixed steps with an append part whose decode has at least 1024 (sequence,
+# range, KV head) workgroups run the decode from a work list (longest ranges
+# first) built by one extra workgroup of the append launch.  40 rows of edge
+# lengths (empty, one token, page and range boundaries) in 64-token ranges,
+# on both decode kernels.
+WORKLIST_LENS = (0, 1, 63, 64, 65, 128, 129, 500, 1000, 2047) * 4
+WORKLIST_CASES = [
+    (WORKLIST_LENS, 32, 8, 128, 32, "bf16"),    # matrix cores, G 4
+    (WORKLIST_LENS, 8, 8, 128, 64, "bf16"),     # vector path, MHA
+    (WORKLIST_LENS, 64, 8, 128, 64, "fp8"),     # matrix cores, 8-bit codes
+    (WORKLIST_LENS, 4, 4, 64, 16, "f32"),       # vector path, fp32
+    (WORKLIST_LENS, 4, 2, 128, 32, "int8"),     # vector path, G 2
+]
+
+
+@pytest.mark.parametrize("case", WORKLIST_CASES)
+def test_mixed_step_work_list_parity_bits_and_graph(case):
+    """The decode of a mixed step run from its work list matches the oracle,
+    equals bit for bit the same step as separate calls (whose decode grid
+    walks (row, range) itself), and so do replays of the step captured as a
+    graph."""
+    spec = spec_of(*case)
+    wl = wk.make_workload(spec, seed=31)
+    kp, vp = sup.oracle_pools(wl)
+    ref, ref_lse = sup.oracle_decode(wl, kp, vp)
+    dw = dev.upload(wl, split_tokens=64)
+    dw.setup()
+    dw.step()
+    torch.cuda.synchronize()
+    check_close(dw.out, ref, spec)
+    check_lse(dw.lse, ref_lse, spec)
+    out0, lse0 = dw.out.clone(), dw.lse.clone()
+    side = torch.cuda.Stream()
+
+    def clear():
+        dw.out.fill_(float("nan"))
+        dw.lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+
+    clear()
+    dw.mixed_step(side_stream=side)
+    torch.cuda.synchronize()
+    assert torch.equal(dw.out, out0) and torch.equal(dw.lse, lse0)
+    g = dw.capture_step(side_stream=side)
+    for rep in range(3):
+        clear()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dw.out, out0) and torch.equal(dw.lse, lse0), f"graph replay {rep}"
+        dw.step()                                   # eager work between replays
+        torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_mixed_step_work_list_full_size_bits(cfg):
+    """At full size, the mixed step (decode from its work list, beside the
+    prefill for the mixed workload) reproduces the separate calls' bits."""
+    wl = wk.make_workload(wk.CONFIGS[cfg])
+    dw = dev.upload(wl)
+    dw.setup()
+    dw.step()
+    torch.cuda.synchronize()
+    ref = [dw.out.clone(), dw.lse.clone()] + ([dw.pf["out"].clone(), dw.pf["lse"].clone()]
+                                              if dw.pf else [])
+    outs = [dw.out, dw.lse] + ([dw.pf["out"], dw.pf["lse"]] if dw.pf else [])
+    for t in outs:
+        t.fill_(float("nan"))
+    dw.mixed_step(side_stream=torch.cuda.Stream())
+    torch.cuda.synchronize()
+    for a, b in zip(outs, ref):
+        assert torch.equal(a, b)
+
+
 # ---------------------------------------------------------- graph replay ----
 @pytest.mark.parametrize("cfg", [1, 5])
 def test_step_graph_replays_match_eager(cfg):
