@@ -315,6 +315,13 @@ def main() -> int:
     # with events in an eager loop after the timed steps (inside a replay or a
     # fused call they cannot be bracketed; with --launch calls the partial's
     # events were recorded inside the timed loop already).
+    # The partial is timed in the order the step's decode used: a one-call
+    # step whose decode has the GPU to itself takes its items from a work
+    # list (longest ranges first), built here once (the lengths do not
+    # change between these calls) instead of inside each step's append.
+    listed = args.launch.endswith("mixed_step") and not wl.num_prefill
+    if listed and wl.num_seqs:
+        dw.build_work_list()
     ev_pf = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
              for _ in range(K)]
     for i in range(K):
@@ -322,7 +329,7 @@ def main() -> int:
         if wl.num_seqs:
             if args.launch != "calls":
                 ev[i][0].record()
-            dw.decode_partial()
+            dw.decode_partial(listed=listed)
             if args.launch != "calls":
                 ev[i][1].record()
             dw.merge()
@@ -388,7 +395,9 @@ def main() -> int:
                    "split_tokens": dw.split_tokens,
                    "prefill_split_tokens": dw.pf["split"] if dw.pf else None,
                    "parallelism": "single GPU",
-                   "launch": args.launch},
+                   "launch": args.launch,
+                   "decode_order": "work list (longest ranges first) when the call is large "
+                                   "enough" if listed else "grid"},
         "seq_steps_per_s": round((wl.num_seqs + wl.num_prefill) / (ms * 1e-3), 1),
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "step_bytes": step_bytes,

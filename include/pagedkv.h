@@ -231,6 +231,35 @@ pkv_status pkv_paged_attn_decode_partial(const pkv_cache_desc* cache,
                                          void* workspace, size_t workspace_bytes,
                                          void* stream);
 
+/* Decode work list for separate calls (pkv_mixed_step builds its own).
+ * pkv_decode_work_list orders the (sequence, context range) work items of a
+ * decode call with these arguments by token count, longest first, into the
+ * work-list area of `workspace` (one single-workgroup kernel on `stream`;
+ * it reads only context_lens).  pkv_paged_attn_decode_partial_listed, with
+ * the same cache, context_lens contents, num_seqs, num_q_heads,
+ * max_context_len, split_tokens and workspace, later on the same stream,
+ * then takes its items in that order, so that the launch ends on its
+ * shortest items; its results are bit for bit those of
+ * pkv_paged_attn_decode_partial.  Calls of fewer than 1024 (sequence, range,
+ * KV head) work items, or needing no workspace, use no list: the builder
+ * then does nothing and the listed pass walks its grid as the plain one.
+ * A list written for other arguments gives wrong results (items outside
+ * the call are skipped, so nothing is accessed out of bounds).  Arguments
+ * and errors as for pkv_paged_attn_decode_partial. */
+pkv_status pkv_decode_work_list(const pkv_cache_desc* cache, const int32_t* context_lens,
+                                int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+                                int32_t split_tokens, void* workspace, size_t workspace_bytes,
+                                void* stream);
+pkv_status pkv_paged_attn_decode_partial_listed(const pkv_cache_desc* cache,
+                                                const void* q, int32_t q_dtype,
+                                                void* out, int32_t out_dtype, float* lse,
+                                                const int32_t* block_tables, int32_t bt_stride,
+                                                const int32_t* context_lens, int32_t num_seqs,
+                                                int32_t num_q_heads, int32_t max_context_len,
+                                                float sm_scale, int32_t split_tokens,
+                                                void* workspace, size_t workspace_bytes,
+                                                void* stream);
+
 /* The log-sum-exp merge pass: for every sequence with more than one range,
  * M = max_s m_s, w_s = exp(m_s - M), out = sum_s w_s acc_s / sum_s w_s l_s,
  * lse = M + ln(sum_s w_s l_s).  Sequences with one range are untouched. */

@@ -110,6 +110,8 @@ _SIGS = {
     "pkv_decode_workspace_bytes": (_SZ, [_P, _I, _I, _I, _I]),
     "pkv_paged_attn_decode": (_I, [_P, _P, _I, _P, _I, _P, _P, _I, _P, _I, _I, _I, _F, _I, _P, _SZ, _P]),
     "pkv_paged_attn_decode_partial": (_I, [_P, _P, _I, _P, _I, _P, _P, _I, _P, _I, _I, _I, _F, _I, _P, _SZ, _P]),
+    "pkv_paged_attn_decode_partial_listed": (_I, [_P, _P, _I, _P, _I, _P, _P, _I, _P, _I, _I, _I, _F, _I, _P, _SZ, _P]),
+    "pkv_decode_work_list": (_I, [_P, _P, _I, _I, _I, _I, _P, _SZ, _P]),
     "pkv_lse_merge": (_I, [_P, _P, _I, _P, _P, _I, _I, _I, _I, _P, _SZ, _P]),
     "pkv_paged_attn_chunked_prefill": (_I, [_P, _P, _I, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I,
                                             _I, _I, _F, _I, _P, _SZ, _P]),
@@ -429,13 +431,27 @@ def pkv_paged_attn_decode_partial(cache: PagedCache, q: torch.Tensor, out: torch
                                   block_tables: torch.Tensor, context_lens: torch.Tensor,
                                   max_context_len: int, sm_scale: float,
                                   lse: Optional[torch.Tensor] = None, split_tokens: int = 0,
-                                  workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+                                  workspace: Optional[torch.Tensor] = None, stream=None,
+                                  listed: bool = False) -> None:
+    """The partial pass; with listed=True, pkv_paged_attn_decode_partial_listed
+    (items in the order of the work list pkv_decode_work_list wrote)."""
     _decode_args(cache, q, out, lse, block_tables, context_lens)
     wp, wb = _ws(workspace)
-    _check(lib().pkv_paged_attn_decode_partial(
-        cache.desc, _ptr(q), _code_of(q), _ptr(out), _code_of(out), _ptr(lse), _ptr(block_tables),
-        block_tables.shape[1], _ptr(context_lens), q.shape[0], q.shape[1], max_context_len,
-        float(sm_scale), split_tokens, wp, wb, _stream(stream)))
+    f = lib().pkv_paged_attn_decode_partial_listed if listed else lib().pkv_paged_attn_decode_partial
+    _check(f(cache.desc, _ptr(q), _code_of(q), _ptr(out), _code_of(out), _ptr(lse),
+             _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), q.shape[0], q.shape[1],
+             max_context_len, float(sm_scale), split_tokens, wp, wb, _stream(stream)))
+
+
+def pkv_decode_work_list(cache: PagedCache, context_lens: torch.Tensor, num_q_heads: int,
+                         max_context_len: int, split_tokens: int = 0,
+                         workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Order a decode call's work items longest first into its workspace."""
+    _i32(context_lens, "context_lens")
+    wp, wb = _ws(workspace)
+    _check(lib().pkv_decode_work_list(cache.desc, _ptr(context_lens), context_lens.shape[0],
+                                      num_q_heads, max_context_len, split_tokens, wp, wb,
+                                      _stream(stream)))
 
 
 def pkv_lse_merge(cache: PagedCache, out: torch.Tensor, context_lens: torch.Tensor,

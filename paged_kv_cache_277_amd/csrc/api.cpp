@@ -550,6 +550,44 @@ pkv_status pkv_paged_attn_decode_partial(const pkv_cache_desc* cache, const void
                     "paged_attn_decode (partial)");
 }
 
+pkv_status pkv_decode_work_list(const pkv_cache_desc* cache, const int32_t* context_lens,
+                                int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+                                int32_t split_tokens, void* workspace, size_t workspace_bytes_in,
+                                void* stream) {
+  pkv::AttnArgs a;
+  // Only the shape arguments matter here: the shared checks get dtypes the
+  // cache supports and a stand-in output pointer, which nothing writes.
+  const int32_t qo = cache && cache->kv_dtype == PKV_F32 ? PKV_F32 : PKV_BF16;
+  pkv_status st = prepare_decode(cache, nullptr, qo, const_cast<int32_t*>(context_lens), qo,
+                                 nullptr, nullptr, 0, context_lens, num_seqs, num_q_heads,
+                                 max_context_len, 1.0f, split_tokens, workspace,
+                                 workspace_bytes_in, false, &a);
+  if (st != PKV_OK) return st;
+  if (!a.ws_acc || !pkv::decode_plan_useful(a)) return PKV_OK;   // the call walks its grid
+  const pkv::DecodeListArgs l{context_lens, a.num_rows, a.split_tokens, a.max_splits,
+                              decode_list_area(a)};
+  return hip_status(pkv::launch_decode_list(l, static_cast<hipStream_t>(stream)),
+                    "decode_work_list");
+}
+
+pkv_status pkv_paged_attn_decode_partial_listed(const pkv_cache_desc* cache, const void* q,
+                                                int32_t q_dtype, void* out, int32_t out_dtype,
+                                                float* lse, const int32_t* block_tables,
+                                                int32_t bt_stride, const int32_t* context_lens,
+                                                int32_t num_seqs, int32_t num_q_heads,
+                                                int32_t max_context_len, float sm_scale,
+                                                int32_t split_tokens, void* workspace,
+                                                size_t workspace_bytes_in, void* stream) {
+  pkv::AttnArgs a;
+  pkv_status st = prepare_decode(cache, q, q_dtype, out, out_dtype, lse, block_tables, bt_stride,
+                                 context_lens, num_seqs, num_q_heads, max_context_len, sm_scale,
+                                 split_tokens, workspace, workspace_bytes_in, true, &a);
+  if (st != PKV_OK) return st;
+  if (a.ws_acc && pkv::decode_plan_useful(a)) a.plan = decode_list_area(a);
+  return hip_status(pkv::launch_decode_partial(a, static_cast<hipStream_t>(stream)),
+                    "paged_attn_decode (partial, listed)");
+}
+
 pkv_status pkv_lse_merge(const pkv_cache_desc* cache, void* out, int32_t out_dtype, float* lse,
                          const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
                          int32_t max_context_len, int32_t split_tokens, const void* workspace,

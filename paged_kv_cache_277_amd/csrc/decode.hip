@@ -29,6 +29,7 @@
 
 #include <type_traits>
 
+#include "decode_list.h"
 #include "pkv_device.h"
 #include "pkv_launch.h"
 
@@ -145,6 +146,7 @@ __global__ __launch_bounds__(256) void decode_partial_vec(AttnArgs a) {
     if (idx >= a.plan[0]) return;
     z = a.plan[2 + 2 * idx];
     item_range = a.plan[3 + 2 * idx];
+    if (z >= a.num_rows || item_range >= a.max_splits) return;   // a list of another call
   }
   int L, btr;
   size_t qrow;
@@ -442,6 +444,11 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(AttnArgs a) {
   if (d == 0 && a.lse) a.lse[(size_t)z * Hq + h] = (M + __log2f(den)) * kLn2;
 }
 
+// The work list on its own (separate calls): one workgroup.
+__global__ __launch_bounds__(256) void decode_list_kernel(DecodeListArgs a) {
+  build_decode_list(a);
+}
+
 template <int KVT, int D>
 hipError_t launch_vec_d(const AttnArgs& a, dim3 grid, hipStream_t s) {
   const int G = a.num_q_heads / a.c.num_kv_heads;
@@ -475,6 +482,11 @@ hipError_t launch_vec_any(const AttnArgs& a, dim3 grid, hipStream_t s) {
 bool decode_plan_useful(const AttnArgs& a) {
   return !a.prefill && a.max_splits > 1 && a.num_rows > 0 &&
          (int64_t)a.num_rows * a.max_splits * a.c.num_kv_heads >= 1024;
+}
+
+hipError_t launch_decode_list(const DecodeListArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(decode_list_kernel, dim3(1), dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 dim3 decode_plan_grid(const AttnArgs& a) {

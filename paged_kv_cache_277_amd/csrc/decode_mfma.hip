@@ -155,6 +155,7 @@ void decode_partial_mfma(AttnArgs a) {
     if (idx >= a.plan[0]) return;
     z = a.plan[2 + 2 * idx];
     item_range = a.plan[3 + 2 * idx];
+    if (z >= a.num_rows || item_range >= a.max_splits) return;   // a list of another call
   }
   const int L = a.context_lens[z];
   const int Hq = a.num_q_heads, Hkv = a.c.num_kv_heads;

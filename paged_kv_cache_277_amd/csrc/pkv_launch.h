@@ -73,6 +73,7 @@ hipError_t launch_lse_merge(const AttnArgs& a, hipStream_t s);
 // launch that reads it, (KV heads, y, z) with y * z >= rows * max_splits.
 bool decode_plan_useful(const AttnArgs& a);
 dim3 decode_plan_grid(const AttnArgs& a);
+hipError_t launch_decode_list(const DecodeListArgs& a, hipStream_t s);   // one workgroup
 hipError_t launch_prefill(const AttnArgs& a, hipStream_t s);
 // Grouped-query decode on the matrix cores (G >= 3, bf16 or fp8 KV).
 bool decode_mfma_supported(const AttnArgs& a);

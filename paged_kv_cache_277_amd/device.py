@@ -98,11 +98,18 @@ class DeviceWorkload:
                                 split_tokens=self.split_tokens, workspace=self.workspace,
                                 stream=stream)
 
-    def decode_partial(self, stream=None) -> None:
+    def decode_partial(self, stream=None, listed: bool = False) -> None:
+        """The partial pass; listed=True takes its items from the work list
+        (build_work_list), the order pkv_mixed_step's decode uses."""
         B.pkv_paged_attn_decode_partial(self.cache, self.q, self.out, self.bt, self.lens,
                                         self.max_len, float(self.wl.sm_scale), lse=self.lse,
                                         split_tokens=self.split_tokens, workspace=self.workspace,
-                                        stream=stream)
+                                        stream=stream, listed=listed)
+
+    def build_work_list(self, stream=None) -> None:
+        B.pkv_decode_work_list(self.cache, self.lens, self.wl.spec.num_q_heads, self.max_len,
+                               split_tokens=self.split_tokens, workspace=self.workspace,
+                               stream=stream)
 
     def merge(self, stream=None) -> None:
         B.pkv_lse_merge(self.cache, self.out, self.lens, self.max_len, lse=self.lse,

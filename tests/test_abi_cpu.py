@@ -160,6 +160,29 @@ def test_decode_rejects_bad_arguments():
     assert _decode(i8, out_dtype=B.PKV_F32) == B.PKV_ERR_UNSUPPORTED
 
 
+def test_work_list_rejections():
+    """pkv_decode_work_list checks its shape arguments like a decode call
+    (no GPU needed: every case fails before anything is launched)."""
+    lib = B.lib()
+    d = _desc(head_dim=128, page_size=64, num_kv_heads=8, num_pages=3000)
+    ws = lib.pkv_decode_workspace_bytes(C.byref(d), 64, 32, 4096, 64)
+    assert ws > 0
+    # workspace too small for the ranges
+    assert lib.pkv_decode_work_list(C.byref(d), FAKE, 64, 32, 4096, 64, FAKE, ws - 1,
+                                    None) == B.PKV_ERR_INVALID_ARG
+    # num_q_heads not a multiple of the KV heads
+    assert lib.pkv_decode_work_list(C.byref(d), FAKE, 64, 33, 4096, 64, FAKE, ws,
+                                    None) != B.PKV_OK
+    # split not a page multiple
+    assert lib.pkv_decode_work_list(C.byref(d), FAKE, 64, 32, 4096, 96, FAKE, ws,
+                                    None) == B.PKV_ERR_INVALID_ARG
+    # no lengths
+    assert lib.pkv_decode_work_list(C.byref(d), None, 64, 32, 4096, 64, FAKE, ws,
+                                    None) == B.PKV_ERR_INVALID_ARG
+    # one range per sequence: no workspace, no list, nothing launched
+    assert lib.pkv_decode_work_list(C.byref(d), FAKE, 64, 32, 64, 0, None, 0, None) == B.PKV_OK
+
+
 def test_workspace_and_split_planning():
     lib = B.lib()
     d = _desc(head_dim=128, page_size=64, num_kv_heads=40, num_pages=3000)

@@ -422,6 +422,13 @@ def test_mixed_step_work_list_parity_bits_and_graph(case):
     dw.mixed_step(side_stream=side)
     torch.cuda.synchronize()
     assert torch.equal(dw.out, out0) and torch.equal(dw.lse, lse0)
+    # separate calls: the list built on its own, the listed partial pass, the merge
+    clear()
+    dw.build_work_list()
+    dw.decode_partial(listed=True)
+    dw.merge()
+    torch.cuda.synchronize()
+    assert torch.equal(dw.out, out0) and torch.equal(dw.lse, lse0)
     g = dw.capture_step(side_stream=side)
     for rep in range(3):
         clear()
