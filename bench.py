@@ -228,7 +228,10 @@ def main() -> int:
                          "whose matrix-core kernel reaches steady clocks only after ~20 ms of "
                          "work; 10 otherwise)")
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
-    ap.add_argument("--split-tokens", type=int, default=0)
+    ap.add_argument("--split-tokens", type=int, default=0,
+                    help="decode context-range size in tokens (0: the library's default)")
+    ap.add_argument("--prefill-split", type=int, default=0,
+                    help="prefill key-range size in tokens (0: the library's default)")
     ap.add_argument("--kv-format", choices=("fp8", "int8"), default=None,
                     help="run the workload with this 8-bit KV format instead (a variant, "
                          "not one of the five workloads)")
@@ -274,7 +277,7 @@ def main() -> int:
           file=sys.stderr, flush=True)
     if args.warmup is None:
         args.warmup = 200 if wl.pf_block_tables is not None else 10
-    dw = dev.upload(wl, "cuda", split_tokens=args.split_tokens)
+    dw = dev.upload(wl, "cuda", split_tokens=args.split_tokens, prefill_split=args.prefill_split)
     dw.setup()
     torch.cuda.synchronize()
     print(f"[bench] uploaded, split_tokens={dw.split_tokens}", file=sys.stderr, flush=True)

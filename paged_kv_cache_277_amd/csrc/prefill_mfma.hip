@@ -32,6 +32,8 @@
 // XCD so those tiles are served from that XCD's L2.
 #include <math.h>
 
+#include <type_traits>
+
 #include "pkv_device.h"
 #include "pkv_launch.h"
 
@@ -42,7 +44,10 @@ constexpr int kWaves = 4;
 constexpr int kNt = 2;                      // 16-row MFMA N-tiles per wave
 constexpr int kRows = 16 * kNt * kWaves;    // rows per workgroup
 constexpr int kTile = 32;                   // keys per tile
-constexpr int kMaxPages = 512;              // block-table entries staged per workgroup
+constexpr int kMaxPages = 512;
+#ifndef PKV_PF_NB
+#define PKV_PF_NB 3
+#endif              // block-table entries staged per workgroup
 
 typedef __bf16 bf16x8_t __attribute__((__vector_size__(16)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -390,6 +395,326 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma(AttnArgs a, int nqb, int 
   }
 }
 
+
+// ---- bf16 caches: K/V tiles loaded straight into LDS ----
+//
+// gfx950's 16-byte global-to-LDS load writes lane l's data at (the
+// instruction's LDS base) + 16 l, so one wave instruction fills 1 KiB of
+// consecutive LDS and no register holds the tile on its way.  Rows are
+// therefore stored unpadded (2D bytes); instead of padding, the 16-byte piece
+// p of row r sits in slot p ^ lds_swz(r), which keeps the K reads (16 rows,
+// one piece) and the V transpose reads (4 rows, a 32-byte span) on distinct
+// banks.  NB tile buffers: while tile i is computed, tiles i+1 .. i+NB-1
+// are in flight, and one barrier per tile both publishes tile i and frees
+// the buffer of tile i-1 for the load of tile i+NB-1.
+
+template <int D>
+__device__ __forceinline__ int lds_swz(int r) {
+  const int s = ((r & 3) << 1) | ((r >> 2) & 1);
+  return D == 128 ? (s | (r & 8)) : s;
+}
+
+// s_waitcnt with only the vector-memory counter constrained (<= n).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier without a memory fence: a fence would also wait for the
+// tiles still in flight.  LDS reads of the previous tile have completed (their
+// results fed the matrix cores before the barrier is reached); the asm
+// statements stop the compiler from moving memory accesses across it.
+__device__ __forceinline__ void bar_nofence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// V^T operands of four 16-column d-tiles: for each, the two 16-key halves
+// (LDS offsets BASE and BASE + HALF from the lane's address).  Written as
+// one asm block that waits for its own reads: the builtin form of this read
+// makes the compiler wait for every global-to-LDS load still in flight.
+template <int BASE, int HALF>
+__device__ __forceinline__ void vt_read4(u32x4 (&va)[4], const uint32_t* addr) {
+  u32x2 a0, b0, a1, b1, a2, b2, a3, b3;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %1, %8 offset:%13\n\t"
+      "ds_read_b64_tr_b16 %2, %9 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %3, %9 offset:%13\n\t"
+      "ds_read_b64_tr_b16 %4, %10 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %5, %10 offset:%13\n\t"
+      "ds_read_b64_tr_b16 %6, %11 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %7, %11 offset:%13\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(a0), "=&v"(b0), "=&v"(a1), "=&v"(b1), "=&v"(a2), "=&v"(b2), "=&v"(a3), "=&v"(b3)
+      : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "i"(BASE), "i"(BASE + HALF));
+  va[0] = u32x4{a0[0], a0[1], b0[0], b0[1]};
+  va[1] = u32x4{a1[0], a1[1], b1[0], b1[1]};
+  va[2] = u32x4{a2[0], a2[1], b2[0], b2[1]};
+  va[3] = u32x4{a3[0], a3[1], b3[0], b3[1]};
+}
+
+template <int D, bool PAGED, int NB>
+__global__ __launch_bounds__(256, 2) void prefill_mfma_lds(AttnArgs a, int nqb, int npg) {
+  static_assert(NB == 3 || NB == 4, "three or four tile buffers");
+  constexpr int KK = D / 32, DT = D / 16;
+  constexpr int ROWB = 2 * D;                      // bytes per bf16 row
+  constexpr int SPR = ROWB / 16;                   // 16-byte slots per row
+  constexpr int RPC = 1024 / ROWB;                 // rows per 1 KiB wave load
+  constexpr int CPW = kTile * ROWB / 1024 / 4;     // K (and V) loads per wave per tile
+  constexpr int NLT = 2 * CPW;                     // loads per thread per tile
+  constexpr int KBYTES = kTile * ROWB;
+  constexpr int STAGE = 2 * KBYTES;                // K then V
+  static_assert(CPW >= 1 && kTile * ROWB == 4096 * CPW, "tile must split evenly over four waves");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NB * STAGE + kMaxPages * 4];
+
+  const int Hq = a.num_q_heads, Hkv = a.c.num_kv_heads, G = Hq / Hkv;
+  // Block order as in prefill_mfma: pair p = (request, KV head) on XCD p % 8,
+  // key range outermost, heaviest query block first.
+  const int b = blockIdx.x;
+  const int xcd = b % 8, k = b / 8;
+  const int per_range = npg * nqb;
+  const int rng = k / per_range, kr = k - rng * per_range;
+  const int pair = (kr / nqb) * 8 + xcd;
+  const int qb_rev = kr % nqb;
+  if (pair >= a.num_rows * Hkv) return;
+  const int j = pair % Hkv, r = pair / Hkv;
+  const int c0 = a.cu_q[r], C = a.cu_q[r + 1] - c0;
+  const int qb = nqb - 1 - qb_rev;
+  const int row0 = qb * kRows;
+  if (row0 >= C * G) return;
+  const int Pr = PAGED ? a.ctx_before[r] : 0;
+  const int last_row = min(C * G, row0 + kRows) - 1;
+  const int kneed = Pr + last_row / G + 1;
+  const int t_begin = rng * a.split_tokens;
+  if (t_begin >= kneed) return;
+  const int kmax = min(kneed, t_begin + a.split_tokens);
+
+  const int lane = threadIdx.x & 63;
+  const int w = uniform(threadIdx.x >> 6);
+  const int g4 = lane >> 4, n = lane & 15;
+  const int wrow0 = row0 + kNt * 16 * w;
+  const int wave_last = min(C * G, wrow0 + kNt * 16) - 1;
+  const int wave_kmax = wave_last >= wrow0 ? Pr + wave_last / G + 1 : 0;
+  const int wave_min_lim = Pr + wrow0 / G;
+  const float smul = a.sm_scale * kLog2e;
+
+  int my_lim[kNt];
+  bool row_ok[kNt];
+  size_t row_off[kNt];
+  u32x4 qb_reg[kNt][KK];
+#pragma unroll
+  for (int nt = 0; nt < kNt; ++nt) {
+    const int my_row = wrow0 + 16 * nt + n;
+    row_ok[nt] = my_row < C * G;
+    const int my_tok = my_row / G, my_head = my_row - my_tok * G;
+    my_lim[nt] = Pr + my_tok;
+    row_off[nt] = ((size_t)(c0 + my_tok) * Hq + (size_t)j * G + my_head) * D;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) qb_reg[nt][kk] = u32x4{0, 0, 0, 0};
+    if (row_ok[nt]) {
+      const uint16_t* q = static_cast<const uint16_t*>(a.q) + row_off[nt];
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) qb_reg[nt][kk] = ld16(q + (D / 4) * g4 + 8 * kk);
+    }
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) settle(qb_reg[nt][kk]);
+  }
+
+  f32x4 o[kNt][DT];
+  f32x4 lsum[kNt];
+  float m[kNt];
+  const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+#pragma unroll
+  for (int nt = 0; nt < kNt; ++nt) {
+#pragma unroll
+    for (int i = 0; i < DT; ++i) o[nt][i] = f32x4{0, 0, 0, 0};
+    m[nt] = -INFINITY;
+    lsum[nt] = f32x4{0, 0, 0, 0};
+  }
+
+  const uint8_t* kp = static_cast<const uint8_t*>(a.c.k_pool);
+  const uint8_t* vp = static_cast<const uint8_t*>(a.c.v_pool);
+  const int ntiles = (kmax - t_begin + kTile - 1) / kTile;
+  const int pshift = a.page_shift;
+  const int pmask = (1 << pshift) - 1;
+
+  int32_t* pages = reinterpret_cast<int32_t*>(smem + NB * STAGE);
+  const int pg0 = t_begin >> pshift;
+  if constexpr (PAGED) {
+    const int32_t* btrow = a.bt + (size_t)r * a.bt_stride;
+    const int npages = ((kmax - 1) >> pshift) - pg0 + 1;
+    for (int i = threadIdx.x; i < npages; i += blockDim.x) pages[i] = btrow[pg0 + i];
+  }
+  __syncthreads();
+
+  // This lane's part of each wave load: row ld_row[i] of the tile, the
+  // swizzled piece that belongs in the lane's slot.
+  int ld_row[CPW];
+  uint32_t ld_pb[CPW];
+#pragma unroll
+  for (int i = 0; i < CPW; ++i) {
+    const int c = w * CPW + i;                     // 1 KiB chunk of the K (and V) tile
+    ld_row[i] = c * RPC + lane / SPR;
+    ld_pb[i] = (uint32_t)(((lane % SPR) ^ lds_swz<D>(ld_row[i])) * 16);
+  }
+  // Loads of tile `it` into buffer `buf`.  Keys past kmax (only in a range's
+  // last tile, all above every row's causal limit) re-read key kmax-1: finite
+  // values whose probability is exactly 0.
+  auto issue = [&](int it, int buf) {
+    const int t0 = t_begin + it * kTile;
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+      const int t = min(t0 + ld_row[i], kmax - 1);
+      size_t off;
+      if constexpr (PAGED) {
+        const int page = pages[(t >> pshift) - pg0];
+        off = ((((size_t)page * Hkv + j) << pshift) | (size_t)(t & pmask)) * ROWB + ld_pb[i];
+      } else {
+        off = ((size_t)(c0 + t) * Hkv + j) * ROWB + ld_pb[i];
+      }
+      uint8_t* kdst = smem + buf * STAGE + (w * CPW + i) * 1024;
+      __builtin_amdgcn_global_load_lds(kp + off, (__attribute__((address_space(3))) void*)kdst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vp + off, (__attribute__((address_space(3))) void*)(kdst + KBYTES), 16, 0, 0);
+    }
+  };
+
+  typedef u32x4 __attribute__((address_space(3))) * lds_u32x4_ptr;
+  __attribute__((address_space(3))) uint8_t* lds = (__attribute__((address_space(3))) uint8_t*)(smem);
+  const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+
+  // Per-lane LDS read offsets (the buffer and 16-row block enter as
+  // constants); the V^T ones are absolute LDS addresses for the asm reads.
+  uint32_t k_off[KK], v_off[DT];
+  {
+    const int sk = lds_swz<D>(n);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) k_off[kk] = n * ROWB + (((g4 * KK + kk) ^ sk) << 4);
+    const int vr = 4 * g4 + (n >> 2);
+    const int sv = lds_swz<D>(vr);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      v_off[dt] = lds_base + vr * ROWB + (((2 * dt + ((n >> 1) & 1)) ^ sv) << 4) + 8 * (n & 1);
+  }
+
+  auto compute = [&](int it, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
+    const int t0 = t_begin + it * kTile;
+    if (t0 >= wave_kmax) return;                  // tile wholly above this wave's diagonal
+    __attribute__((address_space(3))) uint8_t* kl = lds + buf * STAGE;
+    f32x4 s[kNt][2];
+#pragma unroll
+    for (int nt = 0; nt < kNt; ++nt) s[nt][0] = s[nt][1] = f32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const u32x4 ka = *(lds_u32x4_ptr)(kl + blk * 16 * ROWB + k_off[kk]);
+#pragma unroll
+        for (int nt = 0; nt < kNt; ++nt) s[nt][blk] = mfma16(ka, qb_reg[nt][kk], s[nt][blk]);
+      }
+    }
+    const bool diag = t0 + kTile - 1 > wave_min_lim;
+    u32x4 pb[kNt];
+#pragma unroll
+    for (int nt = 0; nt < kNt; ++nt) {
+      float sv[8];
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) sv[4 * blk + rr] = s[nt][blk][rr];
+      if (diag) {
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+            if (t0 + 16 * blk + 4 * g4 + rr > my_lim[nt]) sv[4 * blk + rr] = -INFINITY;
+      }
+      float mx = sv[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
+      if (__any(mx * smul > m[nt] + kSlack)) {
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float mn = fmaxf(m[nt], mx * smul);
+        const float alpha = m[nt] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m[nt] - mn);
+        lsum[nt] *= alpha;
+#pragma unroll
+        for (int i = 0; i < DT; ++i) o[nt][i] *= alpha;
+        m[nt] = mn;
+      }
+      const float msub = m[nt] == -INFINITY ? 0.0f : m[nt];
+      float p[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(sv[i], smul, -msub));
+      pb[nt][0] = pack_bf16x2(p[0], p[1]);
+      pb[nt][1] = pack_bf16x2(p[2], p[3]);
+      pb[nt][2] = pack_bf16x2(p[4], p[5]);
+      pb[nt][3] = pack_bf16x2(p[6], p[7]);
+      lsum[nt] = mfma16(ones, pb[nt], lsum[nt]);
+    }
+#pragma unroll
+    for (int d4 = 0; d4 < DT / 4; ++d4) {
+      u32x4 va[4];
+      vt_read4<buf * STAGE + KBYTES, 16 * ROWB>(va, v_off + 4 * d4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int nt = 0; nt < kNt; ++nt) o[nt][4 * d4 + i] = mfma16(va[i], pb[nt], o[nt][4 * d4 + i]);
+    }
+  };
+
+  // Tile it: wait for its loads (only later tiles may stay in flight), one
+  // barrier, start tile it+NB-1 in the buffer tile it-1 used, compute tile it.
+  auto step = [&](int it, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
+    const int pend = min(ntiles - 1 - it, NB - 2);  // tiles after `it` already issued
+    if (pend == 2) wait_vm<2 * NLT>();
+    else if (pend == 1) wait_vm<NLT>();
+    else wait_vm<0>();
+    bar_nofence();
+    if (it + NB - 1 < ntiles) issue(it + NB - 1, (buf + NB - 1) % NB);
+    compute(it, bufc);
+  };
+
+  for (int i = 0; i < NB - 1; ++i)
+    if (i < ntiles) issue(i, i);
+  for (int it = 0; it < ntiles; it += NB) {
+    step(it, std::integral_constant<int, 0>());
+    if (it + 1 < ntiles) step(it + 1, std::integral_constant<int, 1>());
+    if (it + 2 < ntiles) step(it + 2, std::integral_constant<int, 2>());
+    if constexpr (NB == 4)
+      if (it + 3 < ntiles) step(it + 3, std::integral_constant<int, 3>());
+  }
+
+#pragma unroll
+  for (int nt = 0; nt < kNt; ++nt) {
+    const float lt = lsum[nt][0];
+    const int L = my_lim[nt] + 1;
+    const bool single = L <= a.split_tokens;
+    if (row_ok[nt] && single && rng == 0) {
+      const float inv = 1.0f / lt;
+      uint16_t* out = static_cast<uint16_t*>(a.out) + row_off[nt];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const uint32_t lo = pack_bf16x2(o[nt][dt][0] * inv, o[nt][dt][1] * inv);
+        const uint32_t hi = pack_bf16x2(o[nt][dt][2] * inv, o[nt][dt][3] * inv);
+        *reinterpret_cast<u32x2*>(out + 16 * dt + 4 * g4) = u32x2{lo, hi};
+      }
+      if (g4 == 0 && a.lse) a.lse[row_off[nt] / D] = (m[nt] + __log2f(lt)) * kLn2;
+    } else if (row_ok[nt] && !single && t_begin < L) {
+      const size_t slot = (row_off[nt] / D) * a.max_splits + rng;
+      float* acc = a.ws_acc + slot * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        *reinterpret_cast<f32x4*>(acc + 16 * dt + 4 * g4) = o[nt][dt];
+      if (g4 == 0) { a.ws_ml[slot * 2] = m[nt]; a.ws_ml[slot * 2 + 1] = lt; }
+    }
+  }
+}
+
 }  // namespace
 
 // The block-table slice of one key range must fit the LDS staging area: a
@@ -411,8 +736,14 @@ long long prefill_mfma_grid(const AttnArgs& a) {
 
 template <int KVT, bool PAGED>
 void launch_pf(const AttnArgs& a, dim3 grid, hipStream_t s, int nqb, int npg) {
-  if (a.c.head_dim == 128) hipLaunchKernelGGL((prefill_mfma<KVT, 128, PAGED>), grid, dim3(256), 0, s, a, nqb, npg);
-  else hipLaunchKernelGGL((prefill_mfma<KVT, 64, PAGED>), grid, dim3(256), 0, s, a, nqb, npg);
+  if constexpr (KVT == KV_BF16) {
+    constexpr int NB = PKV_PF_NB;
+    if (a.c.head_dim == 128) hipLaunchKernelGGL((prefill_mfma_lds<128, PAGED, NB>), grid, dim3(256), 0, s, a, nqb, npg);
+    else hipLaunchKernelGGL((prefill_mfma_lds<64, PAGED, NB>), grid, dim3(256), 0, s, a, nqb, npg);
+  } else {
+    if (a.c.head_dim == 128) hipLaunchKernelGGL((prefill_mfma<KVT, 128, PAGED>), grid, dim3(256), 0, s, a, nqb, npg);
+    else hipLaunchKernelGGL((prefill_mfma<KVT, 64, PAGED>), grid, dim3(256), 0, s, a, nqb, npg);
+  }
 }
 
 hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t s) {
