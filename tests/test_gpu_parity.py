@@ -276,6 +276,7 @@ PREFILL_CASES = [
     ((9,), 8, 1, 64, 32, "fp8", (31,), 45),                   # G 8, fp8, head_dim 64
     ((9,), 16, 2, 128, 64, "int8", (64, 1), 70),              # int8 KV
     ((9,), 8, 1, 64, 32, "int8", (31, 100), 45),              # int8, head_dim 64
+    ((9,), 16, 4, 64, 32, "bf16", (0, 37, 250), 90),          # bf16 head_dim 64, ragged ranges
 ]
 
 
@@ -542,6 +543,8 @@ CONTEXT_CASES = [
     ((5, 100, 129), 8, 8, 64, 0),                          # G 1, head_dim 64
     ((257,), 16, 1, 128, 128),                             # G 16
     ((64, 3), 12, 4, 64, 64),                              # G 3
+    ((300, 45), 16, 4, 64, 0),                             # head_dim 64: 1..10 tiles per block, ragged
+    ((300, 45), 16, 4, 64, 128),                           # ranges of 1..4 tiles around the pipeline depth
 ]
 
 
