@@ -562,22 +562,30 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_lds(AttnArgs a, int nqb, 
   }
   // Loads of tile `it` into buffer `buf`.  Keys past kmax (only in a range's
   // last tile, all above every row's causal limit) re-read key kmax-1: finite
-  // values whose probability is exactly 0.
+  // values whose probability is exactly 0.  A wave load's RPC rows are
+  // consecutive and RPC-aligned, so they lie in one page (pages hold at least
+  // 16 tokens; clamped rows fall in the same page, or the whole load is past
+  // kmax): the row base is wave-uniform (scalar registers) and each lane adds
+  // a 32-bit offset.
   auto issue = [&](int it, int buf) {
     const int t0 = t_begin + it * kTile;
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
+      const int tc = uniform(min(t0 + (w * CPW + i) * RPC, kmax - 1));
       const int t = min(t0 + ld_row[i], kmax - 1);
-      size_t off;
+      size_t base;
+      uint32_t lo;
       if constexpr (PAGED) {
-        const int page = pages[(t >> pshift) - pg0];
-        off = ((((size_t)page * Hkv + j) << pshift) | (size_t)(t & pmask)) * ROWB + ld_pb[i];
+        const int page = uniform(pages[(tc >> pshift) - pg0]);
+        base = (((size_t)page * Hkv + j) << pshift) * ROWB;
+        lo = (uint32_t)(t & pmask) * ROWB + ld_pb[i];
       } else {
-        off = ((size_t)(c0 + t) * Hkv + j) * ROWB + ld_pb[i];
+        base = ((size_t)(c0 + tc) * Hkv + j) * ROWB;
+        lo = (uint32_t)(t - tc) * (uint32_t)(Hkv * ROWB) + ld_pb[i];
       }
       uint8_t* kdst = smem + buf * STAGE + (w * CPW + i) * 1024;
-      __builtin_amdgcn_global_load_lds(kp + off, (__attribute__((address_space(3))) void*)kdst, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vp + off, (__attribute__((address_space(3))) void*)(kdst + KBYTES), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(kp + base + lo, (__attribute__((address_space(3))) void*)kdst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vp + base + lo, (__attribute__((address_space(3))) void*)(kdst + KBYTES), 16, 0, 0);
     }
   };
 
