@@ -402,16 +402,25 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma(AttnArgs a, int nqb, int 
 // instruction's LDS base) + 16 l, so one wave instruction fills 1 KiB of
 // consecutive LDS and no register holds the tile on its way.  Rows are
 // therefore stored unpadded (2D bytes); instead of padding, the 16-byte piece
-// p of row r sits in slot p ^ lds_swz(r), which keeps the K reads (16 rows,
-// one piece) and the V transpose reads (4 rows, a 32-byte span) on distinct
-// banks.  NB tile buffers: while tile i is computed, tiles i+1 .. i+NB-1
+// p of row r sits in slot p ^ lds_swz(r), which keeps the K reads and the V
+// transpose reads on distinct banks.  NB tile buffers: while tile i is computed, tiles i+1 .. i+NB-1
 // are in flight, and one barrier per tile both publishes tile i and frees
 // the buffer of tile i-1 for the load of tile i+NB-1.
 
+// Slot permutation of row r (its low 4 bits r3..r0), chosen so that both
+// reads stay on distinct banks whether the LDS serves 128 or 256 bytes per
+// clock: the K reads (ds_read_b128: 8 or 16 lanes per clock, rows n of one
+// 16-row block, one piece) need distinct slots over 8 and over 16 rows; the
+// V transpose reads (ds_read_b64: 16 or 32 lanes, 4 or 8 rows, a 32-byte
+// slot pair each) need distinct pairs over 4 and over 8 rows.
+//   D = 128 (16 slots): s = (r2 ^ r3, r1, r0, r2)   (bits 3..0)
+//   D =  64 ( 8 slots): s = (r0 ^ r2, r1, r2 ^ r3)  (bits 2..0; rows are
+//                        128 bytes, so r0 already separates row pairs)
 template <int D>
 __device__ __forceinline__ int lds_swz(int r) {
-  const int s = ((r & 3) << 1) | ((r >> 2) & 1);
-  return D == 128 ? (s | (r & 8)) : s;
+  const int r0 = r & 1, r1 = (r >> 1) & 1, r2 = (r >> 2) & 1, r3 = (r >> 3) & 1;
+  if constexpr (D == 128) return r2 | (r0 << 1) | (r1 << 2) | ((r2 ^ r3) << 3);
+  else return (r2 ^ r3) | (r1 << 1) | ((r0 ^ r2) << 2);
 }
 
 // s_waitcnt with only the vector-memory counter constrained (<= n).
