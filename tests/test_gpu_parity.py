@@ -576,6 +576,33 @@ def test_context_fmha_parity(case):
     check_lse(lse, ref_lse, spec)
 
 
+def test_context_fmha_full_size_sampled():
+    """Whole-prompt attention at the long-prompt benchmark shape (4 prompts of
+    8192 tokens, 32/8 heads, head_dim 128, the library's default key ranges:
+    rows past the first range combine two partials), checked on sampled rows:
+    tile, range and prompt boundaries plus random rows."""
+    lens, Hq, Hkv, D = (8192, 8192, 8192, 8192), 32, 8, 128
+    (q, k, v), cu = _ctx_inputs(lens, Hq, Hkv, D, 73)
+    print(f"[full-size context] {len(lens)} x {lens[0]} tokens", flush=True)
+    scale = 1.0 / np.sqrt(D)
+    qd, kd, vd = (dev._dev(x, "bf16", "cuda") for x in (q, k, v))
+    out = torch.full_like(qd, float("nan"))
+    lse = torch.full(qd.shape[:2], float("nan"), dtype=torch.float32, device="cuda")
+    cud = dev._dev(cu, "i32", "cuda")
+    ws = B.context_workspace(len(lens), q.shape[0], Hq, Hkv, D, max(lens), 0)
+    B.pkv_context_fmha(qd, kd, vd, out, cud, max(lens), scale, lse=lse, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    local = [0, 1, 31, 32, 1023, 4095, 4096, 4927, 4928, 4929, 8190, 8191]
+    rows = np.unique(np.concatenate([[int(cu[s]) + i for s in (0, 3) for i in local],
+                                     _sample(int(cu[-1]), 8, 74)]))
+    ref, ref_lse = oa.context_attention(q, k, v, "bf16", cu, scale, rows=rows)
+    spec = spec_of((1,), Hq, Hkv, D, 16, "bf16")
+    sel = torch.from_numpy(rows).cuda()
+    check_close(out[sel], ref, spec, "context (full size)")
+    check_lse(lse[sel], ref_lse, spec)
+
+
 def test_context_fmha_bit_identical_to_prefill_with_nothing_cached():
     """The same kernel over contiguous K/V and over pages (whole prompts as
     one chunk, ctx_before = 0, same key ranges) gives the same bits."""
