@@ -193,14 +193,15 @@ def chunk_sweep(args) -> int:
             cu = torch.arange(0, R * c + 1, c, dtype=torch.int32, device="cuda")
             ctx = torch.full((R,), pos, dtype=torch.int32, device="cuda")
             out = torch.empty_like(sq)
-            ws = B.prefill_workspace(cache, R, R * c, Hq, c, pos + c)
-            steps.append((sq, sk, sv, cu, ctx, out, ws, c, pos + c))
+            sp = min(args.prefill_split, (pos + c + 63) // 64 * 64) if args.prefill_split else 0
+            ws = B.prefill_workspace(cache, R, R * c, Hq, c, pos + c, sp)
+            steps.append((sq, sk, sv, cu, ctx, out, ws, c, pos + c, sp))
 
         def run():
-            for sq, sk, sv, cu, ctx, out, ws, c, tot in steps:
+            for sq, sk, sv, cu, ctx, out, ws, c, tot, sp in steps:
                 B.pkv_kv_cache_append(cache, sk, sv, cu, ctx, bt)
                 B.pkv_paged_attn_chunked_prefill(cache, sq, out, cu, ctx, bt, c, tot, scale,
-                                                 workspace=ws)
+                                                 split_tokens=sp, workspace=ws)
         ms = timed(run, args.steps)
         results.append({"chunk": C, "steps": len(steps), "ms": round(ms, 3),
                         "tflops": round(flops / ms / 1e9, 1)})
@@ -208,8 +209,10 @@ def chunk_sweep(args) -> int:
         del steps
     out = torch.empty_like(q)
     cu = torch.arange(0, T + 1, L, dtype=torch.int32, device="cuda")
-    ws = B.context_workspace(R, T, Hq, Hkv, D, L)
-    ms = timed(lambda: B.pkv_context_fmha(q, k, v, out, cu, L, scale, workspace=ws), args.steps)
+    sp = min(args.prefill_split, (L + 63) // 64 * 64) if args.prefill_split else 0
+    ws = B.context_workspace(R, T, Hq, Hkv, D, L, sp)
+    ms = timed(lambda: B.pkv_context_fmha(q, k, v, out, cu, L, scale, split_tokens=sp,
+                                          workspace=ws), args.steps)
     print(json.dumps({"chunk_sweep": results,
                       "context_fmha": {"ms": round(ms, 3), "tflops": round(flops / ms / 1e9, 1)},
                       "config": {"workload": "prefill of 4 x 8192-token prompts, 32/8 heads, "

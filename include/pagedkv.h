@@ -307,9 +307,14 @@ pkv_status pkv_paged_attn_chunked_prefill(const pkv_cache_desc* cache,
                                           int32_t split_tokens, void* workspace,
                                           size_t workspace_bytes, void* stream);
 
-/* Default key range for a prefill batch (a multiple of 64; at least
- * max_total_len, i.e. one range, for F32 caches).  Pure host function;
- * returns 0 on invalid arguments. */
+/* Default key range for a prefill batch (a multiple of 64).  One range
+ * (no partials, no merge) for F32 caches, and for bf16 / 8-bit caches when
+ * even the least work the batch can have — its longest chunk with nothing
+ * cached — keeps the device's workgroup slots busy for twice the longest
+ * row's walk over max_total_len keys (and the block-table slice of that
+ * range fits the kernel's 512-entry copy); otherwise about 3/5 of
+ * max_total_len (at least 1024), so the longest rows are cut in two.  Pure
+ * host function; returns 0 on invalid arguments. */
 int32_t pkv_prefill_split_tokens(const pkv_cache_desc* cache, int32_t num_reqs,
                                  int32_t num_q_heads, int32_t max_chunk_len,
                                  int32_t max_total_len);
@@ -338,7 +343,10 @@ size_t pkv_prefill_workspace_bytes(const pkv_cache_desc* cache, int32_t num_reqs
  * cu_seqlens : device int32[num_seqs+1], cu[0] = 0, every length <= max_seqlen,
  *              cu[num_seqs] = num_tokens
  * split_tokens, workspace: as for pkv_paged_attn_chunked_prefill, with
- *              max_seqlen in place of max_total_len.
+ *              max_seqlen in place of max_total_len; the default (0) takes
+ *              one range when the least work of num_tokens tokens over
+ *              num_seqs prompts (num_tokens^2 / num_seqs squared lengths)
+ *              keeps the device busy for twice the longest row's walk.
  * head_dim 64 or 128, num_q_heads a multiple of num_kv_heads, group <= 16.
  * ------------------------------------------------------------------------ */
 pkv_status pkv_context_fmha(const void* q, const void* k, const void* v, int32_t dtype, void* out,

@@ -238,7 +238,34 @@ int32_t split_for_keys(int32_t max_total, bool one_range) {
   return std::min<int32_t>(one, std::max<int32_t>(1024, part));
 }
 
-int32_t default_prefill_split(const pkv_cache_desc* c, int32_t max_total) {
+// One key range per row — no partials to write and merge — pays once the
+// call has enough work that heaviest-first order balances it anyway: when
+// the least work the call can have (in tiles of 128 rows x 32 keys) keeps
+// every workgroup slot of the device (two per CU, 256 CUs) busy for at
+// least twice the longest item, a row's walk over max_keys keys.  A causal
+// sequence of n tokens at G query heads per KV head costs G n^2 / 8192 tiles
+// per KV head.
+constexpr long long kPrefillSlots = 2LL * 256;
+
+bool one_range_pays(long double min_tiles, int32_t max_keys) {
+  return min_tiles >= 2.0L * kPrefillSlots * ((max_keys + 31) / 32);
+}
+
+long double causal_tiles(long double n_sq, int32_t num_q_heads, int32_t num_kv_heads) {
+  const int32_t G = num_kv_heads > 0 ? num_q_heads / num_kv_heads : 0;
+  return (long double)num_kv_heads * G * n_sq / 8192.0L;
+}
+
+// Chunked prefill: the least work is the longest chunk with nothing cached
+// before it (the host knows neither the other chunks nor the cached lengths).
+// A range's block-table slice must fit the kernel's LDS copy (512 entries).
+int32_t default_prefill_split(const pkv_cache_desc* c, int32_t num_q_heads, int32_t max_chunk,
+                              int32_t max_total) {
+  const int32_t whole = std::max<int32_t>(64, (max_total + 63) / 64 * 64);
+  if (c->kv_dtype != PKV_F32 && whole / c->page_size + 1 <= 512 &&
+      one_range_pays(causal_tiles((long double)max_chunk * max_chunk, num_q_heads,
+                                  c->num_kv_heads), max_total))
+    return whole;
   return split_for_keys(max_total, c->kv_dtype == PKV_F32);
 }
 
@@ -295,7 +322,14 @@ pkv_status prepare_context(const void* q, const void* k, const void* v, int32_t 
   if (need_out) *need_out = 0;
   if (num_seqs == 0 || num_tokens == 0) return PKV_OK;
   if (max_seqlen <= 0) return fail(PKV_ERR_INVALID_ARG, "max_seqlen must be positive");
-  const int32_t split = split_tokens ? split_tokens : split_for_keys(max_seqlen, false);
+  // Whole prompts: num_tokens over num_seqs sequences cost at least
+  // num_tokens^2 / num_seqs (squared lengths, Cauchy-Schwarz).
+  const bool one = one_range_pays(
+      causal_tiles((long double)num_tokens * num_tokens / num_seqs, num_q_heads, num_kv_heads),
+      max_seqlen);
+  const int32_t split = split_tokens ? split_tokens
+                        : one ? std::max<int32_t>(64, (max_seqlen + 63) / 64 * 64)
+                              : split_for_keys(max_seqlen, false);
   if (split % 64 != 0)
     return fail(PKV_ERR_INVALID_ARG, "split_tokens %d is not a positive multiple of 64", split);
   const int32_t ms = ceil_div(max_seqlen, split);
@@ -345,7 +379,9 @@ pkv_status prepare_prefill(const pkv_cache_desc* cache, int32_t q_dtype, int32_t
   if (max_total_len < max_chunk_len)
     return fail(PKV_ERR_INVALID_ARG, "max_total_len %d < max_chunk_len %d", max_total_len,
                 max_chunk_len);
-  const int32_t split = split_tokens ? split_tokens : default_prefill_split(cache, max_total_len);
+  const int32_t split =
+      split_tokens ? split_tokens
+                   : default_prefill_split(cache, num_q_heads, max_chunk_len, max_total_len);
   if (split % 64 != 0)
     return fail(PKV_ERR_INVALID_ARG, "split_tokens %d is not a positive multiple of 64", split);
   const int32_t ms = ceil_div(max_total_len, split);
@@ -639,7 +675,7 @@ int32_t pkv_prefill_split_tokens(const pkv_cache_desc* cache, int32_t num_reqs,
                                  int32_t max_total_len) {
   if (check_cache(cache) != PKV_OK || check_heads(cache, num_q_heads) != PKV_OK) return 0;
   if (num_reqs < 0 || max_chunk_len < 0 || max_total_len < max_chunk_len) return 0;
-  return default_prefill_split(cache, max_total_len);
+  return default_prefill_split(cache, num_q_heads, max_chunk_len, max_total_len);
 }
 
 size_t pkv_prefill_workspace_bytes(const pkv_cache_desc* cache, int32_t num_reqs,

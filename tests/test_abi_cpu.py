@@ -301,6 +301,27 @@ def test_mixed_step_checks_every_part_before_launching():
 
 
 @fake_ptrs
+def test_prefill_one_range_when_the_work_balances():
+    """The default key range is the whole context (no partials, no merge)
+    when the least work a batch can have keeps 512 workgroup slots busy for
+    twice the longest row's walk; otherwise the longest rows are cut."""
+    lib = B.lib()
+    d = _desc(head_dim=128, page_size=32, num_kv_heads=8, num_pages=4000)
+    # mixed step: 4 chunks of 512 over up to 2560 keys -> ranges of 3/5 (1536)
+    assert lib.pkv_prefill_split_tokens(C.byref(d), 4, 32, 512, 2560) == 1536
+    # whole 8192-token prompts (G 4, 8 KV heads): 32 * 8192^2 / 8192 tiles >= 2 * 512 * 256
+    assert lib.pkv_prefill_split_tokens(C.byref(d), 4, 32, 8192, 8192) == 8192
+    assert lib.pkv_prefill_workspace_bytes(C.byref(d), 4, 32768, 32, 8192, 8192, 0) == 0
+    # a short chunk after a long cached context: cut
+    assert lib.pkv_prefill_split_tokens(C.byref(d), 4, 32, 256, 8192) < 8192
+    # page 16: a whole 16384-key context has 1024 pages, more than the kernel's table copy
+    d16 = _desc(head_dim=128, page_size=16, num_kv_heads=8, num_pages=8000)
+    assert lib.pkv_prefill_split_tokens(C.byref(d16), 1, 32, 16384, 16384) < 16384
+    # context attention: 4 x 8192 tokens take one range, 1 x 8192 + 100 short prompts do not
+    assert lib.pkv_context_fmha_workspace_bytes(4, 32768, 32, 8, 128, 8192, 0) == 0
+    assert lib.pkv_context_fmha_workspace_bytes(101, 8192 + 1000, 32, 8, 128, 8192, 0) > 0
+
+
 def test_context_fmha_rejects_on_host_and_plans_workspace():
     lib = B.lib()
 

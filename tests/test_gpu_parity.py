@@ -277,6 +277,7 @@ PREFILL_CASES = [
     ((9,), 16, 2, 128, 64, "int8", (64, 1), 70),              # int8 KV
     ((9,), 8, 1, 64, 32, "int8", (31, 100), 45),              # int8, head_dim 64
     ((9,), 16, 4, 64, 32, "bf16", (0, 37, 250), 90),          # bf16 head_dim 64, ragged ranges
+    ((9,), 8, 2, 128, 16, "bf16", (5, 70), 40),               # bf16 head_dim 128, page 16
 ]
 
 
@@ -576,24 +577,27 @@ def test_context_fmha_parity(case):
     check_lse(lse, ref_lse, spec)
 
 
-def test_context_fmha_full_size_sampled():
+@pytest.mark.parametrize("split", [0, 4096])
+def test_context_fmha_full_size_sampled(split):
     """Whole-prompt attention at the long-prompt benchmark shape (4 prompts of
-    8192 tokens, 32/8 heads, head_dim 128, the library's default key ranges:
-    rows past the first range combine two partials), checked on sampled rows:
-    tile, range and prompt boundaries plus random rows."""
+    8192 tokens, 32/8 heads, head_dim 128): the default (one key range per
+    row) and 4096-key ranges (rows past the first range combine two
+    partials), checked on sampled rows: tile, range and prompt boundaries
+    plus random rows."""
     lens, Hq, Hkv, D = (8192, 8192, 8192, 8192), 32, 8, 128
     (q, k, v), cu = _ctx_inputs(lens, Hq, Hkv, D, 73)
-    print(f"[full-size context] {len(lens)} x {lens[0]} tokens", flush=True)
+    print(f"[full-size context] {len(lens)} x {lens[0]} tokens, split {split}", flush=True)
     scale = 1.0 / np.sqrt(D)
     qd, kd, vd = (dev._dev(x, "bf16", "cuda") for x in (q, k, v))
     out = torch.full_like(qd, float("nan"))
     lse = torch.full(qd.shape[:2], float("nan"), dtype=torch.float32, device="cuda")
     cud = dev._dev(cu, "i32", "cuda")
-    ws = B.context_workspace(len(lens), q.shape[0], Hq, Hkv, D, max(lens), 0)
-    B.pkv_context_fmha(qd, kd, vd, out, cud, max(lens), scale, lse=lse, workspace=ws)
+    ws = B.context_workspace(len(lens), q.shape[0], Hq, Hkv, D, max(lens), split)
+    B.pkv_context_fmha(qd, kd, vd, out, cud, max(lens), scale, lse=lse, split_tokens=split,
+                       workspace=ws)
     torch.cuda.synchronize()
     assert torch.isfinite(out.float()).all()
-    local = [0, 1, 31, 32, 1023, 4095, 4096, 4927, 4928, 4929, 8190, 8191]
+    local = [0, 1, 31, 32, 1023, 4095, 4096, 4097, 4927, 4928, 8190, 8191]
     rows = np.unique(np.concatenate([[int(cu[s]) + i for s in (0, 3) for i in local],
                                      _sample(int(cu[-1]), 8, 74)]))
     ref, ref_lse = oa.context_attention(q, k, v, "bf16", cu, scale, rows=rows)
