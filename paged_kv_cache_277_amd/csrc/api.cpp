@@ -104,21 +104,28 @@ int32_t default_split(const pkv_cache_desc* c, int32_t num_seqs, int32_t num_q_h
   int split;
   if (G >= 3 && c->kv_dtype != PKV_F32) {
     // Matrix-core path: long ranges amortise each work item's start-up,
-    // but the grid must keep ~2048 items.  With only the longest context
+    // but the grid must keep enough items.  With only the longest context
     // known, the expected item count assumes contexts average half of it.
-    // Ranges of 512 tokens up to 1 MiB of K+V per KV head (2048 tokens of
-    // 16-bit, 4096 of 8-bit codes at head_dim 128).
+    // Ranges of 512 tokens up to 1 MiB of K+V per KV head and item for 16-bit
+    // caches (2048 tokens at head_dim 128, while ~2048 items remain) and 2 MiB
+    // for 8-bit codes (8192 tokens, while ~1024 items remain: a decode that
+    // has the GPU to itself takes its items longest first, which balances
+    // fewer, longer items).
     const bool coded = c->kv_dtype == PKV_FP8_E4M3FN || c->kv_dtype == PKV_INT8;
-    const int cap = coded ? 4096 : 2048;
+    const int cap = coded ? 8192 : 2048;
+    const int64_t min_items = coded ? 1024 : 2048;
+    // (A range's block-table slice, at most 512 entries, is staged in LDS.)
     split = 512;
-    while (split < cap && pairs * ceil_div(std::max(1, max_len), 2 * split) / 2 >= 2048) split *= 2;
+    while (split < cap && (2 * split) / c->page_size + 2 <= 512 &&
+           pairs * ceil_div(std::max(1, max_len), 2 * split) / 2 >= min_items)
+      split *= 2;
   } else {
-    // Vector path: 1024 tokens per KV head and item (512 KiB of 16-bit K+V
-    // at head_dim 128; 8-bit codes measured no better with longer ranges);
-    // shorter ranges when the batch would give fewer than ~8 items per CU,
-    // never below 256 tokens (the merge would cost more than the parallelism
-    // gains).
-    split = 1024;
+    // Vector path: 1 MiB of 16-bit K+V per KV head and item (2048 tokens at
+    // head_dim 128), 1024 tokens of other formats (8-bit codes measured no
+    // better with longer ranges); shorter ranges when the batch would give
+    // fewer than ~8 items per CU, never below 256 tokens (the merge would cost
+    // more than the parallelism gains).
+    split = c->kv_dtype == PKV_BF16 ? 2048 : 1024;
     if (c->head_dim == 64) split *= 2;
     const int floor_split = 256;
     while (split / 2 >= floor_split && pairs * ceil_div(std::max(1, max_len), split) < 8 * kNumCUs)
