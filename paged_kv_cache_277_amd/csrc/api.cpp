@@ -273,7 +273,11 @@ int32_t default_prefill_split(const pkv_cache_desc* c, int32_t num_q_heads, int3
       one_range_pays(causal_tiles((long double)max_chunk * max_chunk, num_q_heads,
                                   c->num_kv_heads), max_total))
     return whole;
-  return split_for_keys(max_total, c->kv_dtype == PKV_F32);
+  const int32_t split = split_for_keys(max_total, c->kv_dtype == PKV_F32);
+  if (c->kv_dtype == PKV_F32) return split;
+  // at most 511 pages per range (multiple of 64 tokens)
+  const int32_t cap = std::max<int32_t>(64, 511 * c->page_size / 64 * 64);
+  return std::min(split, cap);
 }
 
 size_t ranges_ws_bytes(int32_t head_dim, int32_t num_q_tokens, int32_t num_q_heads, int32_t ms) {

@@ -336,6 +336,10 @@ def test_prefill_one_range_when_the_work_balances():
     # page 16: a whole 16384-key context has 1024 pages, more than the kernel's table copy
     d16 = _desc(head_dim=128, page_size=16, num_kv_heads=8, num_pages=8000)
     assert lib.pkv_prefill_split_tokens(C.byref(d16), 1, 32, 16384, 16384) < 16384
+    # long contexts on 16-token pages: every default range's block-table slice fits 512 entries
+    for total in (9000, 20000, 65536):
+        sp = lib.pkv_prefill_split_tokens(C.byref(d16), 8, 32, 64, total)
+        assert sp % 64 == 0 and sp // 16 + 1 <= 512, (total, sp)
     # context attention: 4 x 8192 tokens take one range, 1 x 8192 + 100 short prompts do not
     assert lib.pkv_context_fmha_workspace_bytes(4, 32768, 32, 8, 128, 8192, 0) == 0
     assert lib.pkv_context_fmha_workspace_bytes(101, 8192 + 1000, 32, 8, 128, 8192, 0) > 0

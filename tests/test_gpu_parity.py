@@ -278,6 +278,7 @@ PREFILL_CASES = [
     ((9,), 8, 1, 64, 32, "int8", (31, 100), 45),              # int8, head_dim 64
     ((9,), 16, 4, 64, 32, "bf16", (0, 37, 250), 90),          # bf16 head_dim 64, ragged ranges
     ((9,), 8, 2, 128, 16, "bf16", (5, 70), 40),               # bf16 head_dim 128, page 16
+    ((9,), 8, 2, 64, 16, "bf16", (14000,), 20),               # long context, page 16: ranges capped at 511 pages
 ]
 
 
