@@ -291,7 +291,11 @@ pkv_status pkv_lse_merge(const pkv_cache_desc* cache, void* out, int32_t out_dty
  *                 max_chunk_len <= max_total_len <= bt_stride * page_size
  * split_tokens  : key range per work item, a positive multiple of 64; 0
  *                 selects pkv_prefill_split_tokens().  F32 caches take one
- *                 range only (split_tokens >= max_total_len, or 0).
+ *                 range only (split_tokens >= max_total_len, or 0).  With
+ *                 bf16 / 8-bit caches a range spans at most 511 pages
+ *                 (split_tokens / page_size + 1 <= 512); a longer one
+ *                 leaves only the one-range generic path, so several such
+ *                 ranges give PKV_ERR_UNSUPPORTED.
  * workspace     : device scratch of at least pkv_prefill_workspace_bytes(...)
  *                 bytes (NULL when that is 0); contents on entry are ignored.
  * Supported dtypes as for decode.
