@@ -41,15 +41,16 @@ def _threads_used() -> int:
         return 1
 
 
-def measured_traffic(spec_name: str):
+def measured_traffic(spec_name: str, split_tokens: int):
     """HBM bytes per launch of the decode-partial kernel from the committed
     counter record (profiles/traffic.json), or None when the record is for
-    another workload or the kernel's sources changed since it was taken."""
+    another workload or context-range size, or the kernel's sources changed
+    since it was taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         rec = json.load(open(path))
-        if rec.get("workload") != spec_name:
+        if rec.get("workload") != spec_name or rec.get("split_tokens") != split_tokens:
             return None
         h = hashlib.sha256()
         for f in rec["sources"]:
@@ -415,7 +416,7 @@ def main() -> int:
         "roofline": {"bound": "hbm", "kernel": "decode_partial", "achieved": round(part_gbs, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(part_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(spec.name),
+                     "traffic": measured_traffic(spec.name, dw.split_tokens),
                      "kernel_ms": round(part_ms, 5),
                      "kernel_ms_p10_p50_p90": [round(float(np.percentile(part_times, q)), 5)
                                                for q in (10, 50, 90)],

@@ -755,8 +755,11 @@ pkv_status pkv_mixed_step(const pkv_cache_desc* cache, const pkv_append_batch* a
   if ((st = step_events(&ev_fork, &ev_join)) != PKV_OK) return st;
   if ((st = hip_status(hipEventRecord(ev_fork, s), "mixed_step: fork")) != PKV_OK) return st;
   if ((st = hip_status(hipStreamWaitEvent(side, ev_fork, 0), "mixed_step: fork")) != PKV_OK) return st;
-  if ((st = launch_prefill_call(pa, side)) != PKV_OK) return st;   // longer branch first
+  // Decode first: with the direct-to-LDS prefill this packs as well as the
+  // prefill-first order on a warm cache and 4% better from HBM (8B mixed
+  // step: 156 against 163 us with the caches flushed).
   if ((st = launch_decode_call(da, s)) != PKV_OK) return st;
+  if ((st = launch_prefill_call(pa, side)) != PKV_OK) return st;
   if ((st = hip_status(hipEventRecord(ev_join, side), "mixed_step: join")) != PKV_OK) return st;
   return hip_status(hipStreamWaitEvent(s, ev_join, 0), "mixed_step: join");
 }
