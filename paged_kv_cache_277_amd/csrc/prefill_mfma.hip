@@ -754,7 +754,7 @@ long long prefill_mfma_grid(const AttnArgs& a) {
 template <int KVT, bool PAGED>
 void launch_pf(const AttnArgs& a, dim3 grid, hipStream_t s, int nqb, int npg) {
   if constexpr (KVT == KV_BF16) {
-    constexpr int NB = PKV_PF_NB;
+    constexpr int NB = kTileBufs;
     if (a.c.head_dim == 128) hipLaunchKernelGGL((prefill_mfma_lds<128, PAGED, NB>), grid, dim3(256), 0, s, a, nqb, npg);
     else hipLaunchKernelGGL((prefill_mfma_lds<64, PAGED, NB>), grid, dim3(256), 0, s, a, nqb, npg);
   } else {
