@@ -44,10 +44,11 @@ constexpr int kWaves = 4;
 constexpr int kNt = 2;                      // 16-row MFMA N-tiles per wave
 constexpr int kRows = 16 * kNt * kWaves;    // rows per workgroup
 constexpr int kTile = 32;                   // keys per tile
-constexpr int kMaxPages = 512;
-#ifndef PKV_PF_NB
-#define PKV_PF_NB 3
-#endif              // block-table entries staged per workgroup
+constexpr int kMaxPages = 512;              // block-table entries staged per workgroup
+// Tile buffers of the bf16 kernel: three (two tiles in flight) measured better
+// than four, whose 66 KiB of LDS per workgroup crowd out decode workgroups in
+// a mixed step.
+constexpr int kTileBufs = 3;
 
 typedef __bf16 bf16x8_t __attribute__((__vector_size__(16)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
