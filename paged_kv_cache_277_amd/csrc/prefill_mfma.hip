@@ -16,18 +16,21 @@
 // long serial walk; rows whose keys span several ranges leave (m, l, acc)
 // partials that the log-sum-exp merge combines, the same way split decode
 // does.  Each K/V tile is fetched from the pages once per workgroup into LDS
-// and shared by the four waves; loads run three tiles ahead of the compute
-// (register staging, double-buffered LDS), with the range's block-table
-// entries staged in LDS so no load waits on another:
+// and shared by the four waves, with the range's block-table entries staged
+// in LDS so no load waits on another.  Two kernels share this decomposition:
+// prefill_mfma_lds (bf16 caches) loads tiles straight into LDS, two tiles
+// ahead; prefill_mfma (8-bit caches) stages them through registers, three
+// tiles ahead, widening the codes to bf16 on the way.  Both compute
 //
 //   S^T[t][row] = sum_d K[t][d] Q[row][d]    A = K from LDS (16-byte reads),
 //                                            B = Q^T in registers
 //   O^T[d][row] += sum_t V[t][d] P^T[t][row] A = V^T by LDS transpose reads,
 //                                            B = P^T straight from S^T's layout
 //
-// with the operand layouts described in decode_mfma.hip.  LDS rows are
-// padded (K by 16 bytes, V by 32) so that the 16-byte K reads and the
-// transpose reads of V hit distinct banks.  Workgroups that share a
+// with the operand layouts described in decode_mfma.hip.  Bank conflicts of
+// the 16-byte K reads and the transpose reads of V are avoided by padded LDS
+// rows in prefill_mfma (K by 16 bytes, V by 32) and by a slot permutation of
+// unpadded rows in prefill_mfma_lds (see lds_swz).  Workgroups that share a
 // (request, KV head) — and so the same K/V tiles — are mapped to the same
 // XCD so those tiles are served from that XCD's L2.
 #include <math.h>
