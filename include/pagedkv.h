@@ -75,7 +75,7 @@ typedef enum pkv_dtype {
 } pkv_dtype;
 
 /* One layer's paged cache.  Supported: kv_dtype F32, BF16, FP8_E4M3FN or INT8;
- * head_dim 64 or 128; page_size 16, 32 or 64; num_kv_heads >= 1.
+ * head_dim 64 or 128; page_size 16, 32, 64, 128 or 256; num_kv_heads >= 1.
  * k_scale / v_scale: device float[num_kv_heads], required iff kv_dtype is
  * FP8_E4M3FN or INT8 (stored code = encode(x / scale), dequantised value =
  * code * scale; the division in float32; fp8 rounds to nearest even and

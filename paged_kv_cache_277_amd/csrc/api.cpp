@@ -47,8 +47,11 @@ pkv_status check_cache(const pkv_cache_desc* c) {
     return fail(PKV_ERR_INVALID_ARG, "kv_dtype %d is not a pkv_dtype", c->kv_dtype);
   if (c->head_dim != 64 && c->head_dim != 128)
     return fail(PKV_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", c->head_dim);
-  if (c->page_size != 16 && c->page_size != 32 && c->page_size != 64)
-    return fail(PKV_ERR_UNSUPPORTED, "page_size %d (supported: 16, 32, 64)", c->page_size);
+  // Any power of two from 16 (a 16-token tile never straddles two pages) to
+  // 256 tokens.
+  if (c->page_size < 16 || c->page_size > 256 || (c->page_size & (c->page_size - 1)) != 0)
+    return fail(PKV_ERR_UNSUPPORTED, "page_size %d (supported: 16, 32, 64, 128, 256)",
+                c->page_size);
   const bool coded = c->kv_dtype == PKV_FP8_E4M3FN || c->kv_dtype == PKV_INT8;
   if (coded && (!c->k_scale || !c->v_scale))
     return fail(PKV_ERR_INVALID_ARG, "an fp8 or int8 cache needs k_scale and v_scale");

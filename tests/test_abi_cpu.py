@@ -123,7 +123,8 @@ def _decode(desc, q_dtype=B.PKV_BF16, out_dtype=B.PKV_BF16, Hq=4, max_len=64, st
 @pytest.mark.parametrize("kw,status", [
     (dict(head_dim=96), B.PKV_ERR_UNSUPPORTED),
     (dict(page_size=8), B.PKV_ERR_UNSUPPORTED),
-    (dict(page_size=128), B.PKV_ERR_UNSUPPORTED),
+    (dict(page_size=96), B.PKV_ERR_UNSUPPORTED),
+    (dict(page_size=512), B.PKV_ERR_UNSUPPORTED),
     (dict(kv_dtype=7), B.PKV_ERR_INVALID_ARG),
     (dict(k_pool=None), B.PKV_ERR_INVALID_ARG),
     (dict(num_pages=0), B.PKV_ERR_INVALID_ARG),
@@ -318,6 +319,26 @@ def test_decode_default_ranges():
     ]
     for kw, args, want in cases:
         assert lib.pkv_decode_split_tokens(C.byref(_desc(**kw)), *args) == want, (kw, args)
+
+
+def test_default_ranges_on_large_pages_are_page_multiples():
+    """128- and 256-token pages: every default decode range is a multiple of
+    the page (the decode's ranges are whole pages) within the 512-entry
+    block-table slice; prefill ranges stay multiples of 64 keys."""
+    lib = B.lib()
+    for P in (128, 256):
+        for kv in (B.PKV_BF16, B.PKV_FP8_E4M3FN, B.PKV_F32):
+            extra = dict(k_scale=FAKE, v_scale=FAKE) if kv == B.PKV_FP8_E4M3FN else {}
+            d = _desc(head_dim=128, page_size=P, num_kv_heads=8, num_pages=4096, kv_dtype=kv, **extra)
+            for seqs in (1, 7, 64, 512):
+                for Hq in (8, 32, 64):
+                    for max_len in (1, 100, 129, 4097, 65536):
+                        sp = lib.pkv_decode_split_tokens(C.byref(d), seqs, Hq, max_len)
+                        assert sp > 0 and sp % P == 0 and sp // P + 2 <= 512, (P, kv, seqs, Hq, max_len, sp)
+            if kv != B.PKV_F32:
+                for chunk, total in ((64, 64), (512, 2560), (20, 14000), (8192, 8192)):
+                    sp = lib.pkv_prefill_split_tokens(C.byref(d), 4, 32, chunk, total)
+                    assert sp > 0 and sp % 64 == 0 and sp // P + 1 <= 512, (P, chunk, total, sp)
 
 
 def test_prefill_one_range_when_the_work_balances():

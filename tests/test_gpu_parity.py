@@ -105,6 +105,8 @@ APPEND_CASES = [
     ((3, 70, 129), 16, 4, 64, 16, "fp8"),
     ((5, 31, 32, 33, 200), 8, 1, 128, 32, "int8"),
     ((3, 70, 129), 16, 4, 64, 16, "int8"),
+    ((5, 127, 128, 129, 300), 8, 2, 128, 128, "bf16"),   # 128-token pages
+    ((3, 255, 256, 257), 8, 8, 64, 256, "fp8"),          # 256-token pages
 ]
 
 
@@ -186,15 +188,21 @@ DECODE_CASES = [
     ((5, 100, 333), 8, 1, 64, 16, "int8"),                # G 8, D 64, page 16
     ((1, 31, 200), 4, 2, 128, 32, "int8"),                # G 2: int8 on the vector path
     ((7, 33, 64), 4, 4, 64, 16, "int8"),                  # G 1, D 64
+    ((1, 127, 128, 129, 700), 8, 8, 128, 128, "bf16"),    # 128-token pages, MHA (vector path)
+    ((16, 255, 256, 257, 1000), 32, 8, 128, 256, "bf16"), # 256-token pages, G 4 (matrix cores)
+    ((1, 129, 1500), 64, 8, 128, 128, "fp8"),             # 128-token pages, G 8, fp8
+    ((5, 300, 513), 4, 2, 64, 256, "int8"),               # 256-token pages, G 2, int8 (vector)
+    ((3, 200), 4, 4, 64, 128, "f32"),                     # 128-token pages, fp32
 ]
 
 
 @pytest.mark.parametrize("case", DECODE_CASES)
 @pytest.mark.parametrize("split", [0, 64])
 def test_decode_parity_small(case, split):
+    """split 64 cuts contexts into many ranges (one page each for pages of
+    more than 64 tokens: ranges are page multiples)."""
     spec = spec_of(*case)
-    if split and split % spec.page_size:
-        pytest.skip("split must be a page multiple")
+    split = max(split, spec.page_size) if split else 0
     wl = wk.make_workload(spec, seed=101)
     kp, vp = sup.oracle_pools(wl)
     ref, ref_lse = sup.oracle_decode(wl, kp, vp)
@@ -279,6 +287,9 @@ PREFILL_CASES = [
     ((9,), 16, 4, 64, 32, "bf16", (0, 37, 250), 90),          # bf16 head_dim 64, ragged ranges
     ((9,), 8, 2, 128, 16, "bf16", (5, 70), 40),               # bf16 head_dim 128, page 16
     ((9,), 8, 2, 64, 16, "bf16", (14000,), 20),               # long context, page 16: ranges capped at 511 pages
+    ((9,), 16, 4, 128, 128, "bf16", (0, 200), 150),           # 128-token pages, ranges start mid-page
+    ((9,), 8, 2, 64, 256, "fp8", (300,), 70),                 # 256-token pages, fp8
+    ((9,), 8, 8, 128, 256, "bf16", (0, 600), 65),             # 256-token pages, G 1
 ]
 
 
@@ -394,6 +405,8 @@ WORKLIST_CASES = [
     (WORKLIST_LENS, 64, 8, 128, 64, "fp8"),     # matrix cores, 8-bit codes
     (WORKLIST_LENS, 4, 4, 64, 16, "f32"),       # vector path, fp32
     (WORKLIST_LENS, 4, 2, 128, 32, "int8"),     # vector path, G 2
+    (WORKLIST_LENS, 32, 8, 128, 128, "bf16"),   # matrix cores, 128-token pages
+    (WORKLIST_LENS, 8, 8, 128, 256, "bf16"),    # vector path, 256-token pages
 ]
 
 
@@ -407,7 +420,7 @@ def test_mixed_step_work_list_parity_bits_and_graph(case):
     wl = wk.make_workload(spec, seed=31)
     kp, vp = sup.oracle_pools(wl)
     ref, ref_lse = sup.oracle_decode(wl, kp, vp)
-    dw = dev.upload(wl, split_tokens=64)
+    dw = dev.upload(wl, split_tokens=max(64, spec.page_size))   # ranges are whole pages
     dw.setup()
     dw.step()
     torch.cuda.synchronize()
