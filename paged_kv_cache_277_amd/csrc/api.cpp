@@ -109,19 +109,33 @@ int32_t default_split(const pkv_cache_desc* c, int32_t num_seqs, int32_t num_q_h
     // Matrix-core path: long ranges amortise each work item's start-up,
     // but the grid must keep enough items.  With only the longest context
     // known, the expected item count assumes contexts average half of it.
-    // Ranges of 512 tokens up to 1 MiB of K+V per KV head and item for 16-bit
-    // caches (2048 tokens at head_dim 128, while ~2048 items remain) and 2 MiB
-    // for 8-bit codes (8192 tokens, while ~1024 items remain: a decode that
-    // has the GPU to itself takes its items longest first, which balances
-    // fewer, longer items).
-    const bool coded = c->kv_dtype == PKV_FP8_E4M3FN || c->kv_dtype == PKV_INT8;
-    const int cap = coded ? 8192 : 2048;
-    const int64_t min_items = coded ? 1024 : 2048;
     // (A range's block-table slice, at most 512 entries, is staged in LDS.)
+    const bool coded = c->kv_dtype == PKV_FP8_E4M3FN || c->kv_dtype == PKV_INT8;
     split = 512;
-    while (split < cap && (2 * split) / c->page_size + 2 <= 512 &&
-           pairs * ceil_div(std::max(1, max_len), 2 * split) / 2 >= min_items)
-      split *= 2;
+    if (coded) {
+      // 8-bit codes: the longest range, in steps of 1024 tokens up to 16384,
+      // that still leaves about 5/3 items per workgroup slot (three per CU,
+      // 768 in all) when contexts spread evenly up to the longest, i.e.
+      // max_len / (2 split) + 1/2 ranges per sequence and KV head.  A decode
+      // that has the GPU to itself takes its items longest first, which
+      // balances fewer, longer items: on 128 sequences of 1024..16384 tokens
+      // (8 KV heads) this picks 10240, ahead of 8192, 9216, 11264 and 12288.
+      for (int s = 16384; s >= 1024; s -= 1024) {
+        if (s / c->page_size + 2 > 512) continue;
+        const double items =
+            (double)pairs * ((double)std::max(1, max_len) / (2.0 * s) + 0.5);
+        if (items >= 1280.0) {
+          split = s;
+          break;
+        }
+      }
+    } else {
+      // 16-bit caches: ranges of 512 tokens up to 1 MiB of K+V per KV head
+      // and item (2048 tokens at head_dim 128) while ~2048 items remain.
+      while (split < 2048 && (2 * split) / c->page_size + 2 <= 512 &&
+             pairs * ceil_div(std::max(1, max_len), 2 * split) / 2 >= 2048)
+        split *= 2;
+    }
   } else {
     // Vector path: 1 MiB of 16-bit K+V per KV head and item (2048 tokens at
     // head_dim 128), 1024 tokens of other formats (8-bit codes measured no

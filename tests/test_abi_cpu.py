@@ -304,18 +304,23 @@ def test_mixed_step_checks_every_part_before_launching():
 @fake_ptrs
 def test_decode_default_ranges():
     """Default context ranges of the benchmark shapes: about 1 MiB of 16-bit
-    K+V per item on the vector path, 2 MiB of 8-bit codes on the matrix cores
-    (within the 512-entry block-table slice), 512 tokens when the batch has
-    few sequences."""
+    K+V per item on the vector path and the matrix cores; for 8-bit codes the
+    longest range (steps of 1024) leaving ~5/3 items per slot (within the
+    512-entry block-table slice); 512 tokens when the batch has few
+    sequences."""
     lib = B.lib()
     cases = [
         (dict(head_dim=128, page_size=64, num_kv_heads=40, num_pages=3000), (64, 40, 4097), 2048),
         (dict(head_dim=128, page_size=32, num_kv_heads=8, num_pages=9000), (256, 32, 8192), 2048),
         (dict(head_dim=128, page_size=64, num_kv_heads=8, num_pages=20000, kv_dtype=B.PKV_FP8_E4M3FN,
-              k_scale=FAKE, v_scale=FAKE), (128, 64, 16384), 8192),
+              k_scale=FAKE, v_scale=FAKE), (128, 64, 16384), 10240),
         (dict(head_dim=128, page_size=16, num_kv_heads=8, num_pages=90000, kv_dtype=B.PKV_FP8_E4M3FN,
-              k_scale=FAKE, v_scale=FAKE), (128, 64, 16384), 4096),
+              k_scale=FAKE, v_scale=FAKE), (128, 64, 16384), 7168),
         (dict(head_dim=128, page_size=32, num_kv_heads=8, num_pages=9000), (48, 32, 4097), 512),
+        (dict(head_dim=128, page_size=64, num_kv_heads=8, num_pages=20000, kv_dtype=B.PKV_INT8,
+              k_scale=FAKE, v_scale=FAKE), (2, 64, 16384), 512),     # few sequences
+        (dict(head_dim=128, page_size=64, num_kv_heads=8, num_pages=20000, kv_dtype=B.PKV_INT8,
+              k_scale=FAKE, v_scale=FAKE), (32, 64, 16384), 1024),
     ]
     for kw, args, want in cases:
         assert lib.pkv_decode_split_tokens(C.byref(_desc(**kw)), *args) == want, (kw, args)
