@@ -326,14 +326,15 @@ def test_decode_default_ranges():
         assert lib.pkv_decode_split_tokens(C.byref(_desc(**kw)), *args) == want, (kw, args)
 
 
-def test_default_ranges_on_large_pages_are_page_multiples():
-    """128- and 256-token pages: every default decode range is a multiple of
+def test_default_ranges_are_page_multiples_within_the_slice():
+    """Every supported page size: every default decode range is a multiple of
     the page (the decode's ranges are whole pages) within the 512-entry
     block-table slice; prefill ranges stay multiples of 64 keys."""
     lib = B.lib()
-    for P in (128, 256):
-        for kv in (B.PKV_BF16, B.PKV_FP8_E4M3FN, B.PKV_F32):
-            extra = dict(k_scale=FAKE, v_scale=FAKE) if kv == B.PKV_FP8_E4M3FN else {}
+    for P in (16, 32, 64, 128, 256):
+        for kv in (B.PKV_BF16, B.PKV_FP8_E4M3FN, B.PKV_INT8, B.PKV_F32):
+            coded = kv in (B.PKV_FP8_E4M3FN, B.PKV_INT8)
+            extra = dict(k_scale=FAKE, v_scale=FAKE) if coded else {}
             d = _desc(head_dim=128, page_size=P, num_kv_heads=8, num_pages=4096, kv_dtype=kv, **extra)
             for seqs in (1, 7, 64, 512):
                 for Hq in (8, 32, 64):
