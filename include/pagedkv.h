@@ -381,8 +381,11 @@ size_t pkv_context_fmha_workspace_bytes(int32_t num_seqs, int32_t num_tokens,
  * the decode reads HBM while the prefill keeps the matrix cores busy — and
  * `stream` waits for it before the call's work is complete; the fork and
  * join are stream events, so a graph captured from `stream` records all of
- * it.  Both streams belong to the current device.  With side_stream NULL the
- * parts run one after another on `stream`.
+ * it.  Both streams belong to the current device.  With side_stream NULL (or
+ * equal to stream) the parts run one after another on `stream`: append,
+ * decode (partial + merge), then prefill (+ merge); the decode has consumed
+ * its workspace before the prefill writes, so the two parts may then share
+ * one workspace buffer.
  *
  * Decode work list: when the step has an append part and the decode does
  * not run beside a prefill, a decode of at least 1024 (sequence, context
@@ -549,17 +552,24 @@ pkv_status pkv_sched_stats(const void* sched, pkv_sched_counts* out);
  * Utilities
  * ------------------------------------------------------------------------ */
 
-/* Debug check, synchronous on `stream`: copies block_tables and lens to the
- * host and checks 0 <= lens[s] <= bt_stride * page_size and that every entry
- * covering tokens 0..lens[s]-1 is in [0, num_pages).  PKV_ERR_BAD_BLOCK_TABLE
- * names the first offending row.  Device pointers; lens is int32[num_seqs]. */
+/* Debug check of the block-table address map that every kernel above trusts
+ * ("TensorRT-LLM框架解析与高性能推理优化实践" §4.2: get_block_table maps a
+ * sequence's logical pages to physical ones; §6.2: the attention kernel
+ * reaches each token through it, shared prefix pages included).
+ * Synchronous on `stream`: copies block_tables and lens to the host and
+ * checks 0 <= lens[s] <= bt_stride * page_size and that every entry covering
+ * tokens 0..lens[s]-1 is in [0, num_pages).  PKV_ERR_BAD_BLOCK_TABLE names the
+ * first offending row.  Device pointers; lens is int32[num_seqs]. */
 pkv_status pkv_validate_block_tables(const pkv_cache_desc* cache, const int32_t* block_tables,
                                      int32_t bt_stride, const int32_t* lens, int32_t num_seqs,
                                      void* stream);
 
-/* Decode n fp8 e4m3fn codes (device uint8[n], 4-byte aligned) to float
- * (device float[n]) with the device conversion of the matrix-core attention
- * path (fp8 -> bf16, exact). */
+/* The in-kernel dequantisation of the fp8 KV cache on its own
+ * ("TensorRT-LLM框架解析与高性能推理优化实践" §7.2: 8-bit KV codes dequantised
+ * inside the attention kernel): decode n fp8 e4m3fn codes (device uint8[n],
+ * 4-byte aligned) to float (device float[n]) with the conversion the
+ * matrix-core attention kernels use (fp8 -> bf16, exact), so that it can be
+ * checked against the format's definition. */
 pkv_status pkv_fp8_e4m3fn_to_f32(const uint8_t* codes, float* out, int64_t n, void* stream);
 
 #ifdef __cplusplus

@@ -75,14 +75,13 @@ def gather_tokens(pool: np.ndarray, block_table: np.ndarray, length: int,
 
     Token t comes from physical page ``block_table[t // page_size]``, slot
     ``t % page_size`` — the block-table address map of §4.2/§6.2."""
-    Hkv, D = pool.shape[1], pool.shape[3]
-    out = np.empty((length, Hkv, D), dtype=pool.dtype)
-    for t in range(length):
-        page = int(block_table[t // page_size])
-        if page < 0 or page >= pool.shape[0]:
-            raise IndexError(f"token {t}: block-table entry {page} outside the pool")
-        out[t] = pool[page, :, t % page_size, :]
-    return out
+    t = np.arange(length)
+    pages = np.asarray(block_table)[t // page_size].astype(np.int64)
+    bad = (pages < 0) | (pages >= pool.shape[0])
+    if bad.any():
+        first = int(np.argmax(bad))
+        raise IndexError(f"token {first}: block-table entry {int(pages[first])} outside the pool")
+    return pool[pages, :, t % page_size, :]
 
 
 # ---------------------------------------------------------- attention ------

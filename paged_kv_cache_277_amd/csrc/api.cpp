@@ -763,8 +763,11 @@ pkv_status pkv_mixed_step(const pkv_cache_desc* cache, const pkv_append_batch* a
   }
   if (ap && (st = hip_status(pkv::launch_append(aa, s), "mixed_step: append")) != PKV_OK) return st;
   if (!fork) {
-    if (pp && (st = launch_prefill_call(pa, s)) != PKV_OK) return st;
+    // The decode (partial + merge) completes before the prefill starts: its
+    // work list and partials are consumed before the prefill writes its own,
+    // so the two parts may share one workspace here.
     if (dp && (st = launch_decode_call(da, s)) != PKV_OK) return st;
+    if (pp && (st = launch_prefill_call(pa, s)) != PKV_OK) return st;
     return PKV_OK;
   }
   hipEvent_t ev_fork, ev_join;

@@ -146,7 +146,9 @@ __global__ __launch_bounds__(256) void decode_partial_vec(AttnArgs a) {
     if (idx >= a.plan[0]) return;
     z = a.plan[2 + 2 * idx];
     item_range = a.plan[3 + 2 * idx];
-    if (z >= a.num_rows || item_range >= a.max_splits) return;   // a list of another call
+    // (entries of a list written for another call, or overwritten, are
+    // skipped: nothing outside this call's rows and ranges is accessed)
+    if (z < 0 || z >= a.num_rows || item_range < 0 || item_range >= a.max_splits) return;
   }
   int L, btr;
   size_t qrow;
