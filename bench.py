@@ -32,15 +32,6 @@ HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2500.0
 
 
-def _threads_used() -> int:
-    try:
-        from threadpoolctl import threadpool_info
-        n = [i.get("num_threads", 1) for i in threadpool_info()]
-        return max(n) if n else 1
-    except Exception:
-        return 1
-
-
 def measured_traffic(spec_name: str, split_tokens: int):
     """HBM bytes per launch of the decode-partial kernel from the committed
     counter record (profiles/traffic.json), or None when the record is for
@@ -63,11 +54,22 @@ def measured_traffic(spec_name: str, split_tokens: int):
 
 
 def cpu_baseline(wl, budget_s: float = 12.0, budget_1thread_s: float = 4.0) -> dict:
-    """The oracle, as it stands, on the sequences of the workload in order
+    """The oracle, as it stands, over the workload's sequences in order
     (repeating the pass if it is short) until about `budget_s` seconds of
-    decode work; scaled to GB/s of the same algorithmic bytes per sequence
-    the GPU figure uses.  A second, shorter run with the BLAS pools limited to
-    one thread gives the single-core figure."""
+    decode work, scaled to GB/s of the same algorithmic bytes per sequence
+    the GPU figure uses.
+
+    The oracle handles one sequence at a time, so the baseline uses the
+    host's cores by running it on disjoint sequences at once: one worker
+    thread per core this process may run on (at most 16), each with its
+    numerical library limited to one thread.  Sequences go in waves of one
+    per worker; a wave's pages are filled by the oracle's append outside the
+    timed region, then its decodes are timed together (wall clock).  A
+    second, shorter run with a single worker gives the one-core figure."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+
     from oracle import attention as oa
     from paged_kv_cache_277_amd import workloads as wk
 
@@ -75,49 +77,50 @@ def cpu_baseline(wl, budget_s: float = 12.0, budget_1thread_s: float = 4.0) -> d
     kp, vp = wl.poisoned_pool()
     filled = set()
 
-    def run(budget):
-        done, bytes_done, t_total, tokens, passes = 0, 0, 0.0, 0, 0
-        while t_total < budget and passes < 50:
-            passes += 1
-            for b in range(wl.num_seqs):
-                if b not in filled:
-                    owners = {("seq", b)}
-                    rows_s = [i for i, o in enumerate(wl.setup.owners)
-                              if o in owners or o[0] == "prefix"]
-                    rows_t = [i for i, o in enumerate(wl.step.owners)
-                              if o in owners or o[0] == "prefix"]
-                    for batch, rows in ((wl.setup, rows_s), (wl.step, rows_t)):
-                        oa.kv_cache_append(kp, vp, s.kv_dtype, batch.k, batch.v, s.kv_in_dtype,
-                                           batch.cu, batch.start_pos, batch.block_tables,
-                                           wl.k_scale, wl.v_scale, rows=rows)
-                    filled.add(b)
+    def fill(b):
+        if b in filled:
+            return
+        owners = {("seq", b)}
+        for batch in (wl.setup, wl.step):
+            rows = [i for i, o in enumerate(batch.owners) if o in owners or o[0] == "prefix"]
+            oa.kv_cache_append(kp, vp, s.kv_dtype, batch.k, batch.v, s.kv_in_dtype, batch.cu,
+                               batch.start_pos, batch.block_tables, wl.k_scale, wl.v_scale,
+                               rows=rows)
+        filled.add(b)
+
+    def decode(b):
+        oa.paged_attn_decode(wl.q, s.q_dtype, kp, vp, s.kv_dtype, wl.block_tables,
+                             wl.context_lens, wl.sm_scale, wl.k_scale, wl.v_scale,
+                             seqs=np.array([b]))
+
+    def run(budget, workers):
+        order = [b for _ in range(50) for b in range(wl.num_seqs)]
+        done, bytes_done, t_total, tokens = 0, 0, 0.0, 0
+        with threadpool_limits(limits=1), ThreadPoolExecutor(workers) as ex:
+            for w0 in range(0, len(order), workers):
+                wave = order[w0:w0 + workers]
+                list(ex.map(fill, sorted(set(wave) - filled)))
                 t0 = time.perf_counter()
-                oa.paged_attn_decode(wl.q, s.q_dtype, kp, vp, s.kv_dtype, wl.block_tables,
-                                     wl.context_lens, wl.sm_scale, wl.k_scale, wl.v_scale,
-                                     seqs=np.array([b]))
+                list(ex.map(decode, wave))
                 t_total += time.perf_counter() - t0
-                done += 1
-                tokens += int(wl.context_lens[b])
-                bytes_done += wk.decode_bytes(s, wl.context_lens[[b]], unique_prefix=False)
+                done += len(wave)
+                tokens += int(wl.context_lens[wave].sum())
+                bytes_done += sum(wk.decode_bytes(s, wl.context_lens[[b]], unique_prefix=False)
+                                  for b in wave)
                 if t_total >= budget:
                     break
-        return bytes_done / t_total / 1e9, done, passes, tokens, t_total
+        return bytes_done / t_total / 1e9, done, tokens, t_total
 
-    gbs, done, passes, tokens, t_total = run(budget_s)
-    out = {"value": round(gbs, 4), "unit": "GB/s", "cores": _threads_used(), "kind": "oracle",
-           "sample": f"fp64 oracle decode of {done} sequence-queries ({passes} pass(es) over the "
-                     f"{wl.num_seqs} sequences in order, {tokens} context tokens) in "
-                     f"{t_total:.1f} s"}
-    try:
-        from threadpoolctl import threadpool_limits
-    except ImportError:
-        return out
-    with threadpool_limits(limits=1):
-        gbs1, done1, _, tokens1, t1 = run(budget_1thread_s)
-    out["value_1thread"] = round(gbs1, 4)
-    out["sample_1thread"] = (f"the same, BLAS limited to one thread: {done1} sequence-queries "
-                             f"({tokens1} context tokens) in {t1:.1f} s")
-    return out
+    n = max(1, min(16, len(os.sched_getaffinity(0))))
+    gbs, done, tokens, t_total = run(budget_s, n)
+    gbs1, done1, tokens1, t1 = run(budget_1thread_s, 1)
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": n, "kind": "oracle",
+            "sample": f"fp64 oracle decode of {done} sequence-queries in order ({tokens} context "
+                      f"tokens) on {n} worker threads, one sequence each at a time, BLAS at one "
+                      f"thread per worker, {t_total:.1f} s of wall-clock decode",
+            "value_1thread": round(gbs1, 4),
+            "sample_1thread": f"the same on one worker: {done1} sequence-queries ({tokens1} "
+                              f"context tokens) in {t1:.1f} s"}
 
 
 def copy_calibration(args) -> int:
@@ -249,6 +252,8 @@ def main() -> int:
     ap.add_argument("--chunk-sweep", action="store_true",
                     help="instead of the step benchmark: chunked prefill of long prompts at "
                          "several chunk sizes against one context-attention call")
+    ap.add_argument("--cpu-baseline-only", action="store_true",
+                    help="only the CPU oracle baseline of the workload (no GPU): one JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain device copy of known size instead (counter scaling)")
     args = ap.parse_args()
@@ -259,10 +264,19 @@ def main() -> int:
               file=sys.stderr)
         return 2
 
+    from paged_kv_cache_277_amd import workloads as wk
+
+    if args.cpu_baseline_only:
+        spec = (wk.variant(f"{args.workload}-{args.kv_format}") if args.kv_format
+                else wk.CONFIGS[args.workload])
+        wl = wk.make_workload(spec)
+        print(json.dumps({"workload": spec.name, "cpu_baseline": cpu_baseline(wl, args.cpu_budget)}),
+              flush=True)
+        return 0
+
     import torch
 
     from paged_kv_cache_277_amd import device as dev
-    from paged_kv_cache_277_amd import workloads as wk
 
     torch.cuda.set_device(0)
     if args.warmup is None and args.copy_calibration:

@@ -268,7 +268,7 @@ def make_workload(spec: Spec, seed: Optional[int] = None) -> Workload:
     pf_total = [c + spec.prefill_chunk for c in spec.prefill_ctx]
 
     max_len = spec.max_len or int(max([*ctx.tolist(), *pf_total, 1]))
-    stride = max(1, -(-max_len // P))
+    stride = max(1, -(-max_len // P), npre)       # every row lists the whole prefix
 
     # ---- page ids -------------------------------------------------------
     def own_pages(L: int) -> int:

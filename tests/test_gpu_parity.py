@@ -352,6 +352,11 @@ def test_prefill_ranges_loose_bound_and_invariance():
 # runs on a thread pool (tests/_support.py); the 70B-shaped fp8 workload,
 # whose 2.3 GB of codes the oracle encodes by table search, is the slowest
 # (about a minute on 16 cores).
+def _sample(n, k, seed):
+    rng = np.random.default_rng(seed)
+    return np.sort(rng.choice(n, size=min(n, k), replace=False))
+
+
 def _pools_equal(dw, kp, vp, what):
     for name, gpu, ref in (("K", dw.cache.k_pool, kp), ("V", dw.cache.v_pool, vp)):
         got = dev.storage_to_numpy(gpu)

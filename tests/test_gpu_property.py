@@ -1,0 +1,92 @@
+"""Property tier: randomised small shapes, HIP path against the oracle.
+
+Each example draws a whole batch: cache format (fp32, bf16, fp8 e4m3fn,
+int8), head size 64 or 128, page size 16..256, 1..4 KV heads with a query
+group of 1..16, decode lengths biased to the edges (0, 1, a page +- 1, two
+pages +- 1) plus random ones, an optional shared prefix, an optional set
+of prefill chunks after random cached lengths, and the context-range sizes
+of the decode and prefill calls, and the launch (separate calls, or one
+mixed-step call with or without a side stream).  One step (append, decode, prefill) runs
+on the GPU; the pools must equal the oracle's byte for byte and every
+output must meet the format's bar.  (The pages ask for an accuracy check
+after every optimisation step: "4. TensorRT-LLM架构与核心组件…" §4.5.)
+
+The example count is bounded and fixed-seeded; shrinking is off, so the
+first failing example ends the test, and each example prints its draw
+before it runs, so a failure names its case.
+"""
+import numpy as np
+import pytest
+import torch
+
+hyp = pytest.importorskip("hypothesis")
+from hypothesis import HealthCheck, Phase, given, settings, strategies as st  # noqa: E402
+
+from paged_kv_cache_277_amd import device as dev  # noqa: E402
+from paged_kv_cache_277_amd import workloads as wk  # noqa: E402
+from tests import _support as sup  # noqa: E402
+from tests.test_gpu_parity import check_close, check_lse  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+EXAMPLES = 60
+
+
+@st.composite
+def batches(draw):
+    kv = draw(st.sampled_from(["f32", "bf16", "fp8", "int8"]))
+    D = draw(st.sampled_from([64, 128]))
+    P = draw(st.sampled_from([16, 32, 64, 128, 256]))
+    Hkv = draw(st.integers(1, 4))
+    G = draw(st.sampled_from([1, 2, 3, 4, 5, 8, 16]))
+    prefix_pages = draw(st.sampled_from([0, 0, 1, 2])) if P <= 64 else 0
+    edge = st.sampled_from([0, 1, P - 1, P, P + 1, 2 * P - 1, 2 * P + 1])
+    lens = draw(st.lists(st.one_of(edge, st.integers(0, 700)), min_size=1, max_size=6))
+    if prefix_pages:
+        lens = [max(L, 1) for L in lens]        # a prefixed sequence holds at least its token
+    prefill = draw(st.booleans())
+    pf_ctx = tuple(draw(st.lists(st.one_of(st.sampled_from([0, 1, P - 1, P]),
+                                           st.integers(0, 400)), min_size=1, max_size=3))
+                   ) if prefill else ()
+    chunk = draw(st.sampled_from([1, 17, 64, 100])) if prefill else 0
+    # decode ranges: whole pages (0 = the library's default)
+    split = draw(st.sampled_from([0, 1, 2, 4])) * max(P, 16)
+    # prefill ranges: multiples of 64 (one range for fp32 caches)
+    pf_split = 0 if kv == "f32" else draw(st.sampled_from([0, 64, 128, 256]))
+    launch = draw(st.sampled_from(["calls", "mixed_step", "mixed_step_side"]))
+    seed = draw(st.integers(0, 2 ** 31 - 1))
+    return dict(kv=kv, D=D, P=P, Hkv=Hkv, G=G, prefix_pages=prefix_pages, lens=tuple(lens),
+                pf_ctx=pf_ctx, chunk=chunk, split=split, pf_split=pf_split, launch=launch,
+                seed=seed)
+
+
+@settings(max_examples=EXAMPLES, deadline=None, database=None, derandomize=True,
+          phases=[Phase.explicit, Phase.generate],
+          suppress_health_check=list(HealthCheck))
+@given(case=batches())
+def test_random_batches_match_oracle(case):
+    print(f"[property] {case}", flush=True)
+    qd = "f32" if case["kv"] == "f32" else "bf16"
+    spec = wk.custom_spec(case["lens"], num_q_heads=case["Hkv"] * case["G"],
+                          num_kv_heads=case["Hkv"], head_dim=case["D"], page_size=case["P"],
+                          q_dtype=qd, kv_dtype=case["kv"], out_dtype=qd,
+                          shared_prefix_pages=case["prefix_pages"], prefill_ctx=case["pf_ctx"],
+                          prefill_chunk=case["chunk"])
+    wl = wk.make_workload(spec, seed=case["seed"])
+    dw = dev.upload(wl, split_tokens=case["split"], prefill_split=case["pf_split"])
+    dw.setup()
+    if case["launch"] == "calls":
+        dw.step()
+    else:
+        dw.mixed_step(side_stream=torch.cuda.Stream() if case["launch"].endswith("side") else None)
+    torch.cuda.synchronize()
+    kp, vp = sup.oracle_pools(wl)
+    for name, gpu, ref in (("K", dw.cache.k_pool, kp), ("V", dw.cache.v_pool, vp)):
+        assert dev.storage_to_numpy(gpu).tobytes() == ref.tobytes(), f"{name} pool differs"
+    ref, ref_lse = sup.oracle_decode(wl, kp, vp)
+    check_close(dw.out, ref, spec, "decode")
+    check_lse(dw.lse, ref_lse, spec)
+    if dw.pf:
+        pref, plse = sup.oracle_prefill(wl, kp, vp)
+        check_close(dw.pf["out"], pref, spec, "prefill")
+        check_lse(dw.pf["lse"], plse, spec)

@@ -30,18 +30,22 @@ def _check(gpu: torch.Tensor, ref: np.ndarray, what: str):
     assert err.max() <= TOL_MAX and err.mean() <= TOL_MEAN, f"{what}: {err.max():.3g} {err.mean():.3g}"
 
 
+# Shared prefixes ("TensorRT-LLM框架解析与高性能推理优化实践" §4.2 block reuse,
+# §6.2 shared prefixes): whole pages registered once with the scheduler,
+# filled by the library's append, and attached (refcounted) to the requests
+# that name them; those requests start computing after the prefix and, when
+# evicted, recompute from it.
+PREFIXES = {0: 32, 1: 48}          # prefix id -> tokens (2 and 3 pages)
+
+
 @pytest.mark.gpu
+@pytest.mark.parametrize("with_prefix", [False, True])
 @pytest.mark.parametrize("policy", [B.PKV_SCHED_AGGRESSIVE, B.PKV_SCHED_CONSERVATIVE])
-def test_scheduler_driven_steps_match_oracle(policy):
-    num_pages, stride = 24, 24
+def test_scheduler_driven_steps_match_oracle(policy, with_prefix):
+    num_pages = 28 if with_prefix else 24
+    stride = num_pages
     sched = B.Scheduler(num_pages, PAGE, max_batch_size=4, max_num_tokens=96, chunk_size=40,
                         policy=policy)
-    rng = np.random.default_rng(77)
-    reqs = {}
-    for rid in range(7):
-        prompt, max_new = int(rng.integers(20, 110)), int(rng.integers(4, 60))
-        sched.add_request(rid, prompt, max_new)
-        reqs[rid] = wk.request_tensors(5, rid, prompt + max_new, Hq, Hkv, D)
     poison = np.uint16(0x7FC1)                       # bf16 NaN: a stale read shows up
     kp = np.full((num_pages, Hkv, PAGE, D), poison, dtype=np.uint16)
     vp = kp.copy()
@@ -49,12 +53,45 @@ def test_scheduler_driven_steps_match_oracle(policy):
     cache = B.PagedCache(kd, vd)
     side = torch.cuda.Stream()
     scale = 1.0 / np.sqrt(D)
+    prefix_data = {}
+    if with_prefix:
+        for pid, n in PREFIXES.items():
+            pages = sched.add_prefix(pid, n)
+            assert len(pages) == n // PAGE
+            _, pk, pv = wk.request_tensors(6, pid, n, Hq, Hkv, D)
+            prefix_data[pid] = (pk, pv)
+            bt = np.array([pages], dtype=np.int32)
+            cu, st = np.array([0, n], dtype=np.int32), np.zeros(1, dtype=np.int32)
+            B.pkv_validate_block_tables(cache, _i32(bt), _i32(cu[1:]))
+            B.pkv_kv_cache_append(cache, _bf16(pk), _bf16(pv), _i32(cu), _i32(st), _i32(bt))
+            oa.kv_cache_append(kp, vp, "bf16", pk, pv, "bf16", cu, st, bt)
+        torch.cuda.synchronize()
+    rng = np.random.default_rng(77)
+    reqs = {}
+    for rid in range(7):
+        pid = (rid % 3) if with_prefix and rid % 3 < 2 else -1
+        plen = PREFIXES[pid] if pid >= 0 else 0
+        prompt, max_new = plen + int(rng.integers(20, 110)), int(rng.integers(4, 60))
+        sched.add_request(rid, prompt, max_new, pid)
+        q, k, v = wk.request_tensors(5, rid, prompt + max_new, Hq, Hkv, D)
+        if pid >= 0:                                 # the prefix's own tokens come first
+            k[:plen], v[:plen] = prefix_data[pid]
+        reqs[rid] = (q, k, v)
     steps = 0
+    prefixed_attended = 0
+    evicted = []
     while sched.stats()["waiting"] + sched.stats()["running"] > 0:
         steps += 1
         assert steps < 500, "scheduler did not drain"
-        items, _ = sched.schedule()
+        items, ev = sched.schedule()
+        evicted += ev
         a = step_arrays(sched, items, stride)
+        if with_prefix:
+            for i, it in enumerate(items):
+                pid = (it[0] % 3) if it[0] % 3 < 2 else -1
+                if pid >= 0:
+                    assert it[3] >= PREFIXES[pid], "a step writes into a shared prefix"
+                    prefixed_attended += 1
         # this step's tokens: item i appends positions start .. start+n-1
         k_new = np.concatenate([reqs[it[0]][1][it[3]:it[3] + it[4]] for it in items])
         v_new = np.concatenate([reqs[it[0]][2][it[3]:it[3] + it[4]] for it in items])
@@ -101,11 +138,23 @@ def test_scheduler_driven_steps_match_oracle(policy):
             _check(pout, ref, f"step {steps} prefill")
             assert np.abs(plse.cpu().numpy() - rlse).max() <= LSE_TOL
         sched.commit()
-    # the device pages equal the oracle's, byte for byte (append is exact)
+    # the device pages equal the oracle's, byte for byte (append is exact;
+    # the prefix pages were never written after their fill)
     assert np.array_equal(kd.view(torch.int16).cpu().numpy().view(np.uint16), kp)
+    assert np.array_equal(vd.view(torch.int16).cpu().numpy().view(np.uint16), vp)
     st = sched.stats()
+    print(f"[scheduler] policy {policy} prefix {with_prefix}: {steps} steps, "
+          f"{st['preemptions']} preemptions, {prefixed_attended} prefixed items", flush=True)
     if policy == B.PKV_SCHED_AGGRESSIVE:
         assert st["preemptions"] > 0, "the trace should force evictions"
     else:
         assert st["preemptions"] == 0
-    assert st["free_pages"] == num_pages
+    held = sum(n // PAGE for n in PREFIXES.values()) if with_prefix else 0
+    assert st["free_pages"] == num_pages - held
+    if with_prefix:
+        assert prefixed_attended > 0
+        if policy == B.PKV_SCHED_AGGRESSIVE:     # a prefixed request recomputed after eviction
+            assert any(e % 3 < 2 for e in evicted), evicted
+        for pid in PREFIXES:
+            sched.remove_prefix(pid)
+        assert sched.stats()["free_pages"] == num_pages

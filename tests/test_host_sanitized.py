@@ -1,0 +1,192 @@
+"""The host page allocator and step scheduler under AddressSanitizer and
+UndefinedBehaviorSanitizer (no GPU).
+
+csrc/allocator.cpp and csrc/scheduler.cpp are pure host C++.  They are
+built here with g++ -fsanitize=address,undefined (leak checking included)
+into tests/sanitize/host_driver.cpp, a replay driver over the same C ABI.
+The seeded scheduler traces of tests/test_scheduler_cpu.py (which also
+check the library against the scheduling oracle at every step) and seeded
+allocator traces with invalid calls (double free, ids out of range, sharing
+a free page, exhaustion) are recorded against the regular library; the
+sanitized build must give the same answer to every recorded call and exit
+without a sanitizer report.  A multi-threaded allocate / share / free
+stress runs in the sanitized build as well.  (The allocator's contract:
+"TensorRT-LLM框架解析与高性能推理优化实践" §4.2 allocate_blocks / free_blocks,
+§5.2 out of memory as an error.)
+"""
+import os
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+
+from paged_kv_cache_277_amd import binding as B
+from tests import test_scheduler_cpu as tsc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "paged_kv_cache_277_amd", "csrc")
+SAN_ENV = {"ASAN_OPTIONS": "detect_leaks=1:halt_on_error=1:abort_on_error=0",
+           "UBSAN_OPTIONS": "halt_on_error=1:print_stacktrace=1"}
+
+
+@pytest.fixture(scope="module")
+def driver(tmp_path_factory):
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("g++ is not installed")
+    exe = str(tmp_path_factory.mktemp("san") / "host_driver")
+    cmd = [gxx, "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-Wall",
+           f"-I{os.path.join(ROOT, 'include')}",
+           os.path.join(ROOT, "tests", "sanitize", "host_driver.cpp"),
+           os.path.join(CSRC, "allocator.cpp"), os.path.join(CSRC, "scheduler.cpp"),
+           "-pthread", "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    return exe
+
+
+def replay(exe, log):
+    """Feed the recorded commands to the sanitized driver; its answers must
+    equal the recorded ones and no sanitizer may report."""
+    env = dict(os.environ, **SAN_ENV)
+    r = subprocess.run([exe], input="".join(c + "\n" for c, _ in log), capture_output=True,
+                       text=True, env=env, timeout=300)
+    assert r.returncode == 0 and "Sanitizer" not in r.stderr and "runtime error" not in r.stderr, \
+        r.stderr[-4000:]
+    got = r.stdout.splitlines()
+    assert len(got) == len(log), (len(got), len(log))
+    for i, ((cmd, want), g) in enumerate(zip(log, got)):
+        assert g == want, f"call {i} `{cmd}`: sanitized build answered `{g}`, library `{want}`"
+
+
+def _status(fn):
+    try:
+        return fn(), 0
+    except B.PkvError as e:
+        return None, e.status
+
+
+class RecordingScheduler:
+    """B.Scheduler that records every call and its answer in the driver's
+    command format."""
+
+    def __init__(self, inner, cfg, log):
+        self.inner, self.log = inner, log
+        self.page_size = inner.page_size
+        log.append(("S_create " + " ".join(map(str, cfg)), "0"))
+
+    def add_prefix(self, pid, tokens):
+        ids, st = _status(lambda: self.inner.add_prefix(pid, tokens))
+        self.log.append((f"S_prefix {pid} {tokens}", " ".join(map(str, [st] + (ids or [])))))
+        if st:
+            raise B.PkvError(st, "recorded")
+        return ids
+
+    def remove_prefix(self, pid):
+        _, st = _status(lambda: self.inner.remove_prefix(pid))
+        self.log.append((f"S_remove {pid}", str(st)))
+        if st:
+            raise B.PkvError(st, "recorded")
+
+    def add_request(self, rid, prompt, max_new, prefix_id=-1):
+        _, st = _status(lambda: self.inner.add_request(rid, prompt, max_new, prefix_id))
+        self.log.append((f"S_add {rid} {prompt} {max_new} {prefix_id}", str(st)))
+        if st:
+            raise B.PkvError(st, "recorded")
+
+    def schedule(self):
+        res, st = _status(self.inner.schedule)
+        if st:
+            self.log.append(("S_schedule", str(st)))
+            raise B.PkvError(st, "recorded")
+        items, ev = res
+        flat = [x for it in items for x in it]
+        self.log.append(("S_schedule", " ".join(map(str, [0, len(items), *flat, len(ev), *ev]))))
+        return res
+
+    def block_table(self, rid):
+        t = self.inner.block_table(rid)
+        self.log.append((f"S_table {rid}", " ".join(map(str, [len(t), *t]))))
+        return t
+
+    def commit(self):
+        fin = self.inner.commit()
+        self.log.append(("S_commit", " ".join(map(str, [0, len(fin), *fin]))))
+        return fin
+
+    def finish(self, rid):
+        self.inner.finish(rid)
+        self.log.append((f"S_finish {rid}", "0"))
+
+    def query(self, rid):
+        q = self.inner.query(rid)
+        self.log.append((f"S_query {rid}", " ".join(map(str, [0, q["num_tokens"], q["num_computed"],
+                                                              q["generated"], q["num_pages"],
+                                                              q["slot"], q["running"]]))))
+        return q
+
+    def stats(self):
+        st = self.inner.stats()
+        self.log.append(("S_stats", " ".join(map(str, [0, st["waiting"], st["running"],
+                                                       st["free_pages"], st["preemptions"]]))))
+        return st
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("conservative", [False, True])
+def test_scheduler_traces_under_sanitizers(driver, seed, conservative):
+    log = []
+    tsc._run_trace(1000 + seed, conservative,
+                   wrap=lambda inner, cfg: RecordingScheduler(inner, cfg, log))
+    log.append(("S_destroy", "0"))
+    assert len(log) > 50
+    replay(driver, log)
+
+
+def test_allocator_traces_under_sanitizers(driver):
+    rng = np.random.default_rng(2026)
+    log = []
+    for trial in range(20):
+        n_pages = int(rng.integers(1, 40))
+        a = B.PageAllocator(n_pages)
+        log.append((f"A_create {n_pages}", "0"))
+        held = []                                  # one entry per reference
+        for _ in range(200):
+            op = rng.integers(0, 6)
+            if op == 0:
+                n = int(rng.integers(0, n_pages + 3))
+                ids, st = _status(lambda: a.alloc(n))
+                log.append((f"A_alloc {n}", " ".join(map(str, [st] + (ids or [])))))
+                held += ids or []
+            elif op in (1, 2):
+                if held and rng.random() < 0.8:
+                    k = int(rng.integers(1, min(len(held), 6) + 1))
+                    pick = [held[i] for i in rng.choice(len(held), size=k, replace=False)]
+                else:                               # invalid ids or a double free
+                    pick = [int(x) for x in rng.integers(-2, n_pages + 2, size=3)]
+                name = "A_share" if op == 1 else "A_free"
+                fn = a.share if op == 1 else a.free
+                _, st = _status(lambda: fn(pick))
+                log.append((f"{name} {len(pick)} " + " ".join(map(str, pick)), str(st)))
+                if st == 0:
+                    if op == 1:
+                        held += pick
+                    else:
+                        for p in pick:
+                            held.remove(p)
+            elif op == 3:
+                log.append(("A_nfree", str(a.num_free)))
+            elif op == 4:
+                p = int(rng.integers(-1, n_pages + 1))
+                log.append((f"A_ref {p}", str(a.refcount(p))))
+            elif held:
+                _, st = _status(lambda: a.free(list(held)))
+                log.append((f"A_free {len(held)} " + " ".join(map(str, held)), str(st)))
+                if st == 0:
+                    held = []
+        a.close()
+        log.append(("A_destroy", "0"))
+    log.append(("A_threads 8 3000 11", "ok"))
+    replay(driver, log)
