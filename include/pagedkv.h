@@ -24,7 +24,8 @@
  * Conventions for every call below:
  *   - Pointers named as device pointers are HIP device memory owned by the
  *     caller.  The library allocates no device memory and keeps no device state
- *     between calls; scratch space is passed in as `workspace`.
+ *     between calls; scratch space is passed in as `workspace` (the one
+ *     exception: the fixed per-GPU array of pkv_paged_attn_decode_noalloc).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Launch
  *     calls enqueue work and return without synchronizing.
  *   - Host-side checks happen before anything is launched: on a non-OK status
@@ -267,6 +268,34 @@ pkv_status pkv_lse_merge(const pkv_cache_desc* cache, void* out, int32_t out_dty
                          const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
                          int32_t max_context_len, int32_t split_tokens,
                          const void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * paged_attn_decode_noalloc — pkv_paged_attn_decode for callers that cannot
+ * allocate device memory (code under stream capture, tight serving loops,
+ * harnesses that forbid allocation): the same kernels and results, with the
+ * partials kept in a fixed device array of the library
+ * (PKV_NOALLOC_SCRATCH_BYTES per GPU, held from module load until the
+ * process ends) instead of a caller workspace.  The call itself allocates
+ * nothing; its first call on a device looks up that device's array once.
+ *
+ * Arguments, supported types and results as for pkv_paged_attn_decode
+ * without workspace / workspace_bytes.  A call whose partials
+ * (pkv_decode_workspace_bytes with the same arguments) exceed
+ * PKV_NOALLOC_SCRATCH_BYTES returns PKV_ERR_INVALID_ARG and launches nothing
+ * (longer split_tokens need fewer partials).  Nothing in the array needs to
+ * start at zero; it keeps the last call's contents.  Every call on one GPU
+ * shares that GPU's array: calls that overlap in time on one GPU (on
+ * different streams, or from several threads without ordering) race and give
+ * wrong results; calls on one stream are ordered and safe.
+ * ------------------------------------------------------------------------ */
+#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+pkv_status pkv_paged_attn_decode_noalloc(const pkv_cache_desc* cache,
+                                         const void* q, int32_t q_dtype,
+                                         void* out, int32_t out_dtype, float* lse,
+                                         const int32_t* block_tables, int32_t bt_stride,
+                                         const int32_t* context_lens, int32_t num_seqs,
+                                         int32_t num_q_heads, int32_t max_context_len,
+                                         float sm_scale, int32_t split_tokens, void* stream);
 
 /* ------------------------------------------------------------------------ *
  * paged_attn_chunked_prefill — causal attention of context chunks over the

@@ -109,6 +109,7 @@ _SIGS = {
     "pkv_decode_split_tokens": (_I, [_P, _I, _I, _I]),
     "pkv_decode_workspace_bytes": (_SZ, [_P, _I, _I, _I, _I]),
     "pkv_paged_attn_decode": (_I, [_P, _P, _I, _P, _I, _P, _P, _I, _P, _I, _I, _I, _F, _I, _P, _SZ, _P]),
+    "pkv_paged_attn_decode_noalloc": (_I, [_P, _P, _I, _P, _I, _P, _P, _I, _P, _I, _I, _I, _F, _I, _P]),
     "pkv_paged_attn_decode_partial": (_I, [_P, _P, _I, _P, _I, _P, _P, _I, _P, _I, _I, _I, _F, _I, _P, _SZ, _P]),
     "pkv_paged_attn_decode_partial_listed": (_I, [_P, _P, _I, _P, _I, _P, _P, _I, _P, _I, _I, _I, _F, _I, _P, _SZ, _P]),
     "pkv_decode_work_list": (_I, [_P, _P, _I, _I, _I, _I, _P, _SZ, _P]),
@@ -425,6 +426,24 @@ def pkv_paged_attn_decode(cache: PagedCache, q: torch.Tensor, out: torch.Tensor,
                                        _ptr(lse), _ptr(block_tables), block_tables.shape[1],
                                        _ptr(context_lens), q.shape[0], q.shape[1], max_context_len,
                                        float(sm_scale), split_tokens, wp, wb, _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20      # PKV_NOALLOC_SCRATCH_BYTES of include/pagedkv.h
+
+
+def pkv_paged_attn_decode_noalloc(cache: PagedCache, q: torch.Tensor, out: torch.Tensor,
+                                  block_tables: torch.Tensor, context_lens: torch.Tensor,
+                                  max_context_len: int, sm_scale: float,
+                                  lse: Optional[torch.Tensor] = None, split_tokens: int = 0,
+                                  stream=None) -> None:
+    """Decode attention with the partials in the library's fixed per-GPU
+    array: no workspace, no device allocation."""
+    _decode_args(cache, q, out, lse, block_tables, context_lens)
+    _check(lib().pkv_paged_attn_decode_noalloc(cache.desc, _ptr(q), _code_of(q), _ptr(out),
+                                               _code_of(out), _ptr(lse), _ptr(block_tables),
+                                               block_tables.shape[1], _ptr(context_lens),
+                                               q.shape[0], q.shape[1], max_context_len,
+                                               float(sm_scale), split_tokens, _stream(stream)))
 
 
 def pkv_paged_attn_decode_partial(cache: PagedCache, q: torch.Tensor, out: torch.Tensor,
