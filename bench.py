@@ -34,23 +34,28 @@ MFMA_BF16_PEAK_TFS = 2500.0
 
 def measured_traffic(spec_name: str, split_tokens: int):
     """HBM bytes per launch of the decode-partial kernel from the committed
-    counter record (profiles/traffic.json), or None when the record is for
-    another workload or context-range size, or the kernel's sources changed
-    since it was taken."""
+    counter records (profiles/traffic.json, one per workload), or None when
+    no record is for this workload and context-range size, or the kernel's
+    sources changed since it was taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
-        rec = json.load(open(path))
-        if rec.get("workload") != spec_name or rec.get("split_tokens") != split_tokens:
-            return None
-        h = hashlib.sha256()
-        for f in rec["sources"]:
-            h.update(open(os.path.join(ROOT, f), "rb").read())
-        if h.hexdigest() != rec["sources_sha256"]:
-            return None
-        return int(rec["traffic_bytes_per_launch"])
-    except (OSError, KeyError, ValueError):
+        recs = json.load(open(path))
+    except (OSError, ValueError):
         return None
+    for rec in recs if isinstance(recs, list) else [recs]:
+        try:
+            if rec.get("workload") != spec_name or rec.get("split_tokens") != split_tokens:
+                continue
+            h = hashlib.sha256()
+            for f in rec["sources"]:
+                h.update(open(os.path.join(ROOT, f), "rb").read())
+            if h.hexdigest() != rec["sources_sha256"]:
+                return None
+            return int(rec["traffic_bytes_per_launch"])
+        except (OSError, KeyError, ValueError):
+            return None
+    return None
 
 
 def cpu_baseline(wl, budget_s: float = 12.0, budget_1thread_s: float = 4.0) -> dict:
@@ -226,82 +231,28 @@ def chunk_sweep(args) -> int:
     return 0
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=None,
-                    help="untimed steps first (default: 200 for a step with a prefill part, "
-                         "whose matrix-core kernel reaches steady clocks only after ~20 ms of "
-                         "work; 10 otherwise)")
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
-    ap.add_argument("--split-tokens", type=int, default=0,
-                    help="decode context-range size in tokens (0: the library's default)")
-    ap.add_argument("--prefill-split", type=int, default=0,
-                    help="prefill key-range size in tokens (0: the library's default)")
-    ap.add_argument("--kv-format", choices=("fp8", "int8"), default=None,
-                    help="run the workload with this 8-bit KV format instead (a variant, "
-                         "not one of the five workloads)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--launch", choices=("mixed_step", "calls", "graph", "graph_mixed_step"),
-                    default="mixed_step",
-                    help="mixed_step: one pkv_mixed_step call per step, prefill on a second "
-                         "stream; calls: append, decode and prefill calls one after another; "
-                         "graph / graph_mixed_step: replays of those captured as a HIP graph")
-    ap.add_argument("--chunk-sweep", action="store_true",
-                    help="instead of the step benchmark: chunked prefill of long prompts at "
-                         "several chunk sizes against one context-attention call")
-    ap.add_argument("--cpu-baseline-only", action="store_true",
-                    help="only the CPU oracle baseline of the workload (no GPU): one JSON line")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="time a plain device copy of known size instead (counter scaling)")
-    args = ap.parse_args()
-
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: the decode path shards by sequence or KV head "
-              "with no exchange, and this build runs on a single MI355X (use --gpus 1).",
-              file=sys.stderr)
-        return 2
-
-    from paged_kv_cache_277_amd import workloads as wk
-
-    if args.cpu_baseline_only:
-        spec = (wk.variant(f"{args.workload}-{args.kv_format}") if args.kv_format
-                else wk.CONFIGS[args.workload])
-        wl = wk.make_workload(spec)
-        print(json.dumps({"workload": spec.name, "cpu_baseline": cpu_baseline(wl, args.cpu_budget)}),
-              flush=True)
-        return 0
-
+def measure(spec, args, warmup, split_tokens: int, prefill_split: int):
+    """Time `args.steps` steps of one workload (after `warmup` untimed ones)
+    in the launch form `args.launch`; returns (JSON line without the CPU
+    baseline, the generated workload)."""
     import torch
 
     from paged_kv_cache_277_amd import device as dev
+    from paged_kv_cache_277_amd import workloads as wk
 
-    torch.cuda.set_device(0)
-    if args.warmup is None and args.copy_calibration:
-        args.warmup = 2
-    if args.warmup is None and args.chunk_sweep:
-        args.warmup = 10            # matrix-core work: steady clocks after ~20 ms
-    if args.copy_calibration:
-        return copy_calibration(args)
-    if args.chunk_sweep:
-        return chunk_sweep(args)
-    spec = (wk.variant(f"{args.workload}-{args.kv_format}") if args.kv_format
-            else wk.CONFIGS[args.workload])
     t0 = time.perf_counter()
     wl = wk.make_workload(spec)
     print(f"[bench] workload {spec.name}: generated in {time.perf_counter() - t0:.1f} s",
           file=sys.stderr, flush=True)
-    if args.warmup is None:
-        args.warmup = 200 if wl.pf_block_tables is not None else 10
-    dw = dev.upload(wl, "cuda", split_tokens=args.split_tokens, prefill_split=args.prefill_split)
+    if warmup is None:
+        warmup = 200 if wl.pf_block_tables is not None else 10
+    dw = dev.upload(wl, "cuda", split_tokens=split_tokens, prefill_split=prefill_split)
     dw.setup()
     torch.cuda.synchronize()
     print(f"[bench] uploaded, split_tokens={dw.split_tokens}", file=sys.stderr, flush=True)
 
     side = torch.cuda.Stream() if args.launch.endswith("mixed_step") else None
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         if side is not None:
             dw.mixed_step(side_stream=side)
         else:
@@ -315,6 +266,7 @@ def main() -> int:
     graph = dw.capture_step(side_stream=side) if args.launch.startswith("graph") else None
     torch.cuda.synchronize()
     start.record()
+    t_host = time.perf_counter()
     for i in range(K):
         if graph is not None:
             graph.replay()
@@ -329,6 +281,7 @@ def main() -> int:
             ev[i][1].record()
             dw.merge()
         dw.prefill()
+    host_us = (time.perf_counter() - t_host) / K * 1e6
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / K
@@ -401,7 +354,7 @@ def main() -> int:
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": K,
-        "warmup": args.warmup,
+        "warmup": warmup,
         "ms_per_step": round(ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -420,6 +373,9 @@ def main() -> int:
                    "decode_order": "work list (longest ranges first) when the call is large "
                                    "enough" if listed else "grid"},
         "seq_steps_per_s": round((wl.num_seqs + wl.num_prefill) / (ms * 1e-3), 1),
+        # host time to enqueue one step (the launch loop without its final
+        # synchronisation): above ms_per_step the step is launch-bound
+        "host_us_per_step": round(host_us, 2),
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "step_bytes": step_bytes,
         "cold_cache": {"ms_median": round(cold_med, 5),
@@ -446,6 +402,82 @@ def main() -> int:
                            "tflops": round(flops / (pf_med * 1e-3) / 1e12, 1),
                            "mfma_frac": round(flops / (pf_med * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4),
                            "note": "kernel plus its range merge, timed alone"}
+    return line, wl
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps first (default: 200 for a step with a prefill part, "
+                         "whose matrix-core kernel reaches steady clocks only after ~20 ms of "
+                         "work; 10 otherwise)")
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--split-tokens", type=int, default=0,
+                    help="decode context-range size in tokens (0: the library's default)")
+    ap.add_argument("--prefill-split", type=int, default=0,
+                    help="prefill key-range size in tokens (0: the library's default)")
+    ap.add_argument("--kv-format", choices=("fp8", "int8"), default=None,
+                    help="run the workload with this 8-bit KV format instead (a variant, "
+                         "not one of the five workloads)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="default workload only: skip the 70B-shaped fp8 decode timed beside it")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--launch", choices=("mixed_step", "calls", "graph", "graph_mixed_step"),
+                    default="mixed_step",
+                    help="mixed_step: one pkv_mixed_step call per step, prefill on a second "
+                         "stream; calls: append, decode and prefill calls one after another; "
+                         "graph / graph_mixed_step: replays of those captured as a HIP graph")
+    ap.add_argument("--chunk-sweep", action="store_true",
+                    help="instead of the step benchmark: chunked prefill of long prompts at "
+                         "several chunk sizes against one context-attention call")
+    ap.add_argument("--cpu-baseline-only", action="store_true",
+                    help="only the CPU oracle baseline of the workload (no GPU): one JSON line")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="time a plain device copy of known size instead (counter scaling)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the decode path shards by sequence or KV head "
+              "with no exchange, and this build runs on a single MI355X (use --gpus 1).",
+              file=sys.stderr)
+        return 2
+
+    from paged_kv_cache_277_amd import workloads as wk
+
+    if args.cpu_baseline_only:
+        spec = (wk.variant(f"{args.workload}-{args.kv_format}") if args.kv_format
+                else wk.CONFIGS[args.workload])
+        wl = wk.make_workload(spec)
+        print(json.dumps({"workload": spec.name, "cpu_baseline": cpu_baseline(wl, args.cpu_budget)}),
+              flush=True)
+        return 0
+
+    import torch
+
+    from paged_kv_cache_277_amd import device as dev
+
+    torch.cuda.set_device(0)
+    if args.warmup is None and args.copy_calibration:
+        args.warmup = 2
+    if args.warmup is None and args.chunk_sweep:
+        args.warmup = 10            # matrix-core work: steady clocks after ~20 ms
+    if args.copy_calibration:
+        return copy_calibration(args)
+    if args.chunk_sweep:
+        return chunk_sweep(args)
+    spec = (wk.variant(f"{args.workload}-{args.kv_format}") if args.kv_format
+            else wk.CONFIGS[args.workload])
+    line, wl = measure(spec, args, args.warmup, args.split_tokens, args.prefill_split)
+    if args.workload == 2 and not args.kv_format and not args.no_secondary:
+        # The decode bar applies to the largest batch by bytes (this one) and
+        # the largest by context, the 70B-shaped fp8 batch: timed the same way.
+        second, _ = measure(wk.CONFIGS[4], args, None, 0, 0)
+        keep = ("value", "unit", "ms_per_step", "hbm_frac", "seq_steps_per_s", "step_bytes",
+                "config", "roofline", "cold_cache", "dtype")
+        line["secondary"] = {k: second[k] for k in keep}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
     print(json.dumps(line), flush=True)
