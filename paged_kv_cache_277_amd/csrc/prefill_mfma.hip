@@ -469,7 +469,43 @@ __device__ __forceinline__ void vt_read4(u32x4 (&va)[4], const uint32_t* addr) {
   va[3] = u32x4{a3[0], a3[1], b3[0], b3[1]};
 }
 
-template <int D, bool PAGED, int NB>
+// V^T operands of eight 16-column d-tiles (16 transpose reads, one wait).
+template <int BASE, int HALF>
+__device__ __forceinline__ void vt_read8(u32x4 (&va)[8], const uint32_t* addr) {
+  u32x2 a0, b0, a1, b1, a2, b2, a3, b3, a4, b4, a5, b5, a6, b6, a7, b7;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %16 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %1, %16 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %2, %17 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %3, %17 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %4, %18 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %5, %18 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %6, %19 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %7, %19 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %8, %20 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %9, %20 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %10, %21 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %11, %21 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %12, %22 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %13, %22 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %14, %23 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %15, %23 offset:%25\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(a0), "=&v"(b0), "=&v"(a1), "=&v"(b1), "=&v"(a2), "=&v"(b2), "=&v"(a3), "=&v"(b3),
+        "=&v"(a4), "=&v"(b4), "=&v"(a5), "=&v"(b5), "=&v"(a6), "=&v"(b6), "=&v"(a7), "=&v"(b7)
+      : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "v"(addr[4]), "v"(addr[5]),
+        "v"(addr[6]), "v"(addr[7]), "i"(BASE), "i"(BASE + HALF));
+  va[0] = u32x4{a0[0], a0[1], b0[0], b0[1]};
+  va[1] = u32x4{a1[0], a1[1], b1[0], b1[1]};
+  va[2] = u32x4{a2[0], a2[1], b2[0], b2[1]};
+  va[3] = u32x4{a3[0], a3[1], b3[0], b3[1]};
+  va[4] = u32x4{a4[0], a4[1], b4[0], b4[1]};
+  va[5] = u32x4{a5[0], a5[1], b5[0], b5[1]};
+  va[6] = u32x4{a6[0], a6[1], b6[0], b6[1]};
+  va[7] = u32x4{a7[0], a7[1], b7[0], b7[1]};
+}
+
+template <int D, bool PAGED, int NB, bool HOIST>
 __global__ __launch_bounds__(256, 2) void prefill_mfma_lds(AttnArgs a, int nqb, int npg) {
   static_assert(NB == 3 || NB == 4, "three or four tile buffers");
   constexpr int KK = D / 32, DT = D / 16;
@@ -625,6 +661,22 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_lds(AttnArgs a, int nqb, 
     const int t0 = t_begin + it * kTile;
     if (t0 >= wave_kmax) return;                  // tile wholly above this wave's diagonal
     __attribute__((address_space(3))) uint8_t* kl = lds + buf * STAGE;
+    // HOIST: the tile's K fragments are all read before its first MFMA (one
+    // round of LDS latency instead of one per pair of fragments), and its
+    // V^T fragments in one batch after the softmax.  That shortens each
+    // workgroup's chain of waits, which decides a launch of about one round
+    // of workgroups; with several rounds, the compiler's interleaving of
+    // reads and MFMAs lets the two waves of a SIMD overlap better and is
+    // kept.
+    u32x4 ka[2][KK];
+    if constexpr (HOIST) {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+          ka[blk][kk] = *(lds_u32x4_ptr)(kl + blk * 16 * ROWB + k_off[kk]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     f32x4 s[kNt][2];
 #pragma unroll
     for (int nt = 0; nt < kNt; ++nt) s[nt][0] = s[nt][1] = f32x4{0, 0, 0, 0};
@@ -632,9 +684,9 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_lds(AttnArgs a, int nqb, 
     for (int blk = 0; blk < 2; ++blk) {
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        const u32x4 ka = *(lds_u32x4_ptr)(kl + blk * 16 * ROWB + k_off[kk]);
+        if constexpr (!HOIST) ka[blk][kk] = *(lds_u32x4_ptr)(kl + blk * 16 * ROWB + k_off[kk]);
 #pragma unroll
-        for (int nt = 0; nt < kNt; ++nt) s[nt][blk] = mfma16(ka, qb_reg[nt][kk], s[nt][blk]);
+        for (int nt = 0; nt < kNt; ++nt) s[nt][blk] = mfma16(ka[blk][kk], qb_reg[nt][kk], s[nt][blk]);
       }
     }
     const bool diag = t0 + kTile - 1 > wave_min_lim;
@@ -676,14 +728,23 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_lds(AttnArgs a, int nqb, 
       pb[nt][3] = pack_bf16x2(p[6], p[7]);
       lsum[nt] = mfma16(ones, pb[nt], lsum[nt]);
     }
+    if constexpr (HOIST && DT == 8) {
+      u32x4 va[DT];
+      vt_read8<buf * STAGE + KBYTES, 16 * ROWB>(va, v_off);
 #pragma unroll
-    for (int d4 = 0; d4 < DT / 4; ++d4) {
-      u32x4 va[4];
-      vt_read4<buf * STAGE + KBYTES, 16 * ROWB>(va, v_off + 4 * d4);
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+        for (int nt = 0; nt < kNt; ++nt) o[nt][dt] = mfma16(va[dt], pb[nt], o[nt][dt]);
+    } else {
 #pragma unroll
-        for (int nt = 0; nt < kNt; ++nt) o[nt][4 * d4 + i] = mfma16(va[i], pb[nt], o[nt][4 * d4 + i]);
+      for (int d4 = 0; d4 < DT / 4; ++d4) {
+        u32x4 va[4];
+        vt_read4<buf * STAGE + KBYTES, 16 * ROWB>(va, v_off + 4 * d4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int nt = 0; nt < kNt; ++nt) o[nt][4 * d4 + i] = mfma16(va[i], pb[nt], o[nt][4 * d4 + i]);
+      }
     }
   };
 
@@ -755,12 +816,23 @@ long long prefill_mfma_grid(const AttnArgs& a) {
   return (pairs + 7) / 8 * 8 * nqb * a.max_splits;
 }
 
+// Launches of at most this many workgroups (about one round of the
+// device's two workgroups per CU, counting the ones that exit at once) take
+// the hoisted-read schedule of the bf16 kernel.
+constexpr long long kHoistMaxGrid = 1024;
+
 template <int KVT, bool PAGED>
 void launch_pf(const AttnArgs& a, dim3 grid, hipStream_t s, int nqb, int npg) {
   if constexpr (KVT == KV_BF16) {
     constexpr int NB = kTileBufs;
-    if (a.c.head_dim == 128) hipLaunchKernelGGL((prefill_mfma_lds<128, PAGED, NB>), grid, dim3(256), 0, s, a, nqb, npg);
-    else hipLaunchKernelGGL((prefill_mfma_lds<64, PAGED, NB>), grid, dim3(256), 0, s, a, nqb, npg);
+    const bool hoist = grid.x <= kHoistMaxGrid;
+    if (a.c.head_dim == 128) {
+      if (hoist) hipLaunchKernelGGL((prefill_mfma_lds<128, PAGED, NB, true>), grid, dim3(256), 0, s, a, nqb, npg);
+      else hipLaunchKernelGGL((prefill_mfma_lds<128, PAGED, NB, false>), grid, dim3(256), 0, s, a, nqb, npg);
+    } else {
+      if (hoist) hipLaunchKernelGGL((prefill_mfma_lds<64, PAGED, NB, true>), grid, dim3(256), 0, s, a, nqb, npg);
+      else hipLaunchKernelGGL((prefill_mfma_lds<64, PAGED, NB, false>), grid, dim3(256), 0, s, a, nqb, npg);
+    }
   } else {
     if (a.c.head_dim == 128) hipLaunchKernelGGL((prefill_mfma<KVT, 128, PAGED>), grid, dim3(256), 0, s, a, nqb, npg);
     else hipLaunchKernelGGL((prefill_mfma<KVT, 64, PAGED>), grid, dim3(256), 0, s, a, nqb, npg);

@@ -315,6 +315,42 @@ def test_prefill_parity_small(case, psplit):
     check_close(dw.out, dref, spec, "decode")
 
 
+@pytest.mark.parametrize("D", [128, 64])
+@pytest.mark.parametrize("psplit", [0, 128])
+def test_prefill_schedules_agree(D, psplit):
+    """The bf16 prefill kernel reads a tile's LDS operands in one of two
+    orders, chosen by the launch's workgroup count.  The same requests with
+    128 empty ones added (their workgroups exit at once) cross the threshold;
+    the real rows must come out bit for bit the same, and match the oracle."""
+    spec = spec_of((9,), 16, 4, D, 32, "bf16", prefill_ctx=(0, 70, 300), prefill_chunk=96)
+    wl = wk.make_workload(spec, seed=47)
+    dw = dev.upload(wl, prefill_split=psplit)
+    dw.setup()
+    dw.append_step()
+    p = dw.pf
+    kp, vp = sup.oracle_pools(wl)
+    ref, ref_lse = sup.oracle_prefill(wl, kp, vp)
+    outs = []
+    for extra in (0, 128):
+        R = wl.num_prefill + extra
+        cu = torch.cat([p["cu"], p["cu"][-1:].repeat(extra)])
+        ctx = torch.cat([p["ctx"], torch.zeros(extra, dtype=torch.int32, device="cuda")])
+        bt = torch.cat([p["bt"], torch.full((extra, p["bt"].shape[1]), -1, dtype=torch.int32,
+                                            device="cuda")])
+        ws = B.prefill_workspace(dw.cache, R, p["q"].shape[0], spec.num_q_heads, p["max_chunk"],
+                                 p["max_total"], psplit)
+        out = torch.full_like(p["out"], float("nan"))
+        lse = torch.full_like(p["lse"], float("nan"))
+        B.pkv_paged_attn_chunked_prefill(dw.cache, p["q"], out, cu, ctx, bt, p["max_chunk"],
+                                         p["max_total"], float(wl.sm_scale), lse=lse,
+                                         split_tokens=psplit, workspace=ws)
+        torch.cuda.synchronize()
+        check_close(out, ref, spec, f"prefill with {extra} empty requests")
+        check_lse(lse, ref_lse, spec)
+        outs.append((out, lse))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
 def test_prefill_ranges_loose_bound_and_invariance():
     """A loose max_total_len bound (more ranges than any row needs) gives the
     same rows as the exact one; range sizes change only rounding."""
