@@ -1,5 +1,5 @@
-// Paged decode attention: split-K partial pass (vector path) and the
-// log-sum-exp merge.
+// Paged decode attention: split-K partial pass (vector path), the decode
+// work list and the launch dispatch (the range merge is in merge.hip).
 //
 // Method: the query attends every cached token of its sequence; the kernel
 // reaches each token's K/V through the block table (page = bt[t / P], slot
@@ -371,81 +371,6 @@ __global__ __launch_bounds__(256) void decode_partial_vec(AttnArgs a) {
   }
 }
 
-// Merge: one wave per (row, query head).  Lanes first take one context range
-// each (the (m, l) pairs: max and weighted sum by wave reductions), then
-// cover head_dim and sum the weighted accumulators, four ranges per batch of
-// independent loads.
-// Log-sum-exp merge of per-range partials:
-//   M = max_s m_s,  w_s = exp2(m_s - M),  out = sum_s w_s acc_s / sum_s w_s l_s,
-//   lse = (M + log2 sum_s w_s l_s) ln 2      (m in log2 units)
-// Every thread owns one 16-byte chunk of one head's output: a workgroup
-// covers 256 / (D/4) heads of one row (8 at D = 128).  The grid is (row,
-// head group) for decode and (chunk row, head group, request) for prefill,
-// so a prefill workgroup reads its request's offsets directly.  A thread
-// reads its head's (m, l) pairs (the same
-// 8-byte words for the whole head, served from cache), forms the weights in
-// registers, then streams that head's partial accumulators — contiguous
-// [ranges][D] — four ranges at a time.  No LDS and no barrier: the chain per
-// thread is one round trip for (m, l) and one per four ranges.
-template <int D>
-__device__ __forceinline__ void store4(float* o, size_t i, f32x4 v) {
-  *reinterpret_cast<f32x4*>(o + i) = v;
-}
-template <int D>
-__device__ __forceinline__ void store4(uint16_t* o, size_t i, f32x4 v) {
-  *reinterpret_cast<u32x2*>(o + i) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-}
-
-template <typename OT, int D>
-__global__ __launch_bounds__(256) void lse_merge_kernel(AttnArgs a) {
-  constexpr int C4 = D / 4;                      // 16-byte chunks per head
-  constexpr int HPW = 256 / C4;                  // heads per workgroup
-  const int h = blockIdx.y * HPW + threadIdx.x / C4;
-  const int d = 4 * (threadIdx.x % C4);
-  const int Hq = a.num_q_heads, ms = a.max_splits;
-  if (h >= Hq) return;
-  int z, L;
-  if (a.prefill) {
-    // Chunk row i of request r is packed row cu_q[r] + i, at absolute
-    // position ctx_before[r] + i: it attends that many keys plus itself.
-    const int r = blockIdx.z, i = blockIdx.x;
-    const int c0 = a.cu_q[r], c1 = a.cu_q[r + 1], pr = a.ctx_before ? a.ctx_before[r] : 0;
-    if (i >= c1 - c0) return;
-    z = c0 + i;
-    L = pr + i + 1;
-  } else {
-    z = blockIdx.x;
-    L = a.context_lens[z];
-  }
-  const int n = min((L + a.split_tokens - 1) / a.split_tokens, ms);
-  if (n <= 1) return;
-  const size_t slot0 = ((size_t)z * Hq + h) * ms;
-  const f32x2* ml = reinterpret_cast<const f32x2*>(a.ws_ml) + slot0;
-  float M = -INFINITY;
-  for (int s = 0; s < n; ++s) M = fmaxf(M, ml[s][0]);
-  const float* acc = a.ws_acc + slot0 * D + d;
-  f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f};
-  float den = 0.0f;
-  for (int s0 = 0; s0 < n; s0 += 4) {
-    f32x4 v[4];
-    f32x2 mlv[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int ss = min(s0 + u, n - 1);         // clamped duplicates get weight 0
-      v[u] = *reinterpret_cast<const f32x4*>(acc + (size_t)ss * D);
-      mlv[u] = ml[ss];
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float wgt = s0 + u < n ? __builtin_amdgcn_exp2f(mlv[u][0] - M) : 0.0f;
-      den = fmaf(mlv[u][1], wgt, den);
-      o += v[u] * wgt;
-    }
-  }
-  store4<D>(static_cast<OT*>(a.out), ((size_t)z * Hq + h) * D + d, o * (1.0f / den));
-  if (d == 0 && a.lse) a.lse[(size_t)z * Hq + h] = (M + __log2f(den)) * kLn2;
-}
-
 // The work list on its own (separate calls): one workgroup.
 __global__ __launch_bounds__(256) void decode_list_kernel(DecodeListArgs a) {
   build_decode_list(a);
@@ -502,24 +427,6 @@ hipError_t launch_decode_partial(const AttnArgs& a, hipStream_t s) {
   if (decode_mfma_supported(a)) return launch_decode_partial_mfma(a, s);
   const dim3 grid = a.plan ? decode_plan_grid(a) : dim3(a.c.num_kv_heads, a.num_rows, a.max_splits);
   return launch_vec_any(a, grid, s);
-}
-
-hipError_t launch_lse_merge(const AttnArgs& a, hipStream_t s) {
-  const int rows = a.prefill ? a.num_tokens : a.num_rows;
-  if (a.num_rows == 0 || rows == 0 || a.max_splits <= 1) return hipSuccess;
-  const bool f32 = a.c.kv_dtype == KV_F32;
-  const int hpw = 256 / (a.c.head_dim / 4);
-  const int groups = (a.num_q_heads + hpw - 1) / hpw;
-  const dim3 grid = a.prefill ? dim3(a.max_chunk, groups, a.num_rows) : dim3(rows, groups);
-  const dim3 block(256);
-  if (a.c.head_dim == 64) {
-    if (f32) hipLaunchKernelGGL((lse_merge_kernel<float, 64>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((lse_merge_kernel<uint16_t, 64>), grid, block, 0, s, a);
-  } else {
-    if (f32) hipLaunchKernelGGL((lse_merge_kernel<float, 128>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((lse_merge_kernel<uint16_t, 128>), grid, block, 0, s, a);
-  }
-  return hipGetLastError();
 }
 
 // Chunked prefill.  bf16 queries go to the matrix-core kernel; the generic
