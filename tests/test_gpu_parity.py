@@ -193,6 +193,10 @@ DECODE_CASES = [
     ((1, 129, 1500), 64, 8, 128, 128, "fp8"),             # 128-token pages, G 8, fp8
     ((5, 300, 513), 4, 2, 64, 256, "int8"),               # 256-token pages, G 2, int8 (vector)
     ((3, 200), 4, 4, 64, 128, "f32"),                     # 128-token pages, fp32
+    # with split 64: rows of 3, 4, 5, 5 and 1 ranges, across the merge's
+    # one-round limit of four ranges (vector path, then matrix cores)
+    ((192, 256, 257, 320, 1), 8, 2, 128, 64, "bf16"),
+    ((192, 256, 257, 320, 1), 16, 4, 128, 32, "bf16"),
 ]
 
 
