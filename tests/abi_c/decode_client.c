@@ -15,6 +15,12 @@
  *   q.bin bt.bin lens.bin         decode query (bf16), block tables, lengths
  * Outputs: kpool_out.bin vpool_out.bin out.bin (bf16) lse.bin (float).
  *
+ * With a file pfmeta.txt (num_reqs num_q_tokens max_chunk_len max_total_len
+ * pf_bt_stride) and pfq.bin pfcu.bin pfctx.bin pfbt.bin beside them, the
+ * three parts (append, decode, chunked prefill) run instead as one
+ * pkv_mixed_step call with the prefill on a second stream, filled in the
+ * library's structs; pfout.bin (bf16) and pflse.bin (float) are written too.
+ *
  * Exit status 0 on success; every library status and runtime error is checked
  * and reported with pkv_last_error(). */
 #include <hip/hip_runtime_api.h>
@@ -38,6 +44,14 @@ static void hip_check(hipError_t e, const char* what) {
 
 static void pkv_check(pkv_status s, const char* what) {
   if (s != PKV_OK) die(what, pkv_last_error());
+}
+
+static int exists(const char* name) {
+  char path[4096];
+  snprintf(path, sizeof path, "%s/%s", g_dir, name);
+  FILE* f = fopen(path, "rb");
+  if (f) fclose(f);
+  return f != NULL;
 }
 
 static void* read_file(const char* name, size_t* size) {
@@ -124,11 +138,8 @@ int main(int argc, char** argv) {
   const int32_t* cu = (const int32_t*)to_device("cu.bin", NULL);
   const int32_t* start = (const int32_t*)to_device("start.bin", NULL);
   const int32_t* stepbt = (const int32_t*)to_device("stepbt.bin", NULL);
-  pkv_check(pkv_kv_cache_append(&cache, knew, vnew, in_dtype, cu, start, stepbt, step_stride,
-                                step_rows, step_tokens, NULL),
-            "pkv_kv_cache_append");
 
-  /* decode */
+  /* decode operands */
   size_t q_bytes;
   const void* q = to_device("q.bin", &q_bytes);
   const int32_t* bt = (const int32_t*)to_device("bt.bin", NULL);
@@ -140,15 +151,103 @@ int main(int argc, char** argv) {
   const size_t ws_bytes = pkv_decode_workspace_bytes(&cache, seqs, hq, max_len, 0);
   void* ws = NULL;
   if (ws_bytes > 0) hip_check(hipMalloc(&ws, ws_bytes), "hipMalloc workspace");
-  pkv_check(pkv_paged_attn_decode(&cache, q, PKV_BF16, out, PKV_BF16, lse, bt, bt_stride, lens,
-                                  seqs, hq, max_len, sm_scale, 0, ws, ws_bytes, NULL),
-            "pkv_paged_attn_decode");
+
+  const int mixed = exists("pfmeta.txt");
+  void* pfout = NULL;
+  float* pflse = NULL;
+  size_t pfq_bytes = 0;
+  int num_reqs = 0, pf_tokens = 0;
+  if (!mixed) {
+    pkv_check(pkv_kv_cache_append(&cache, knew, vnew, in_dtype, cu, start, stepbt, step_stride,
+                                  step_rows, step_tokens, NULL),
+              "pkv_kv_cache_append");
+    pkv_check(pkv_paged_attn_decode(&cache, q, PKV_BF16, out, PKV_BF16, lse, bt, bt_stride, lens,
+                                    seqs, hq, max_len, sm_scale, 0, ws, ws_bytes, NULL),
+              "pkv_paged_attn_decode");
+  } else {
+    char* pm = (char*)read_file("pfmeta.txt", &n);
+    pm = (char*)realloc(pm, n + 1);
+    pm[n] = 0;
+    int max_chunk, max_total, pf_stride;
+    if (sscanf(pm, "%d %d %d %d %d", &num_reqs, &pf_tokens, &max_chunk, &max_total, &pf_stride) != 5)
+      die("pfmeta.txt", "5 fields expected");
+    free(pm);
+    const void* pfq = to_device("pfq.bin", &pfq_bytes);
+    const int32_t* pfcu = (const int32_t*)to_device("pfcu.bin", NULL);
+    const int32_t* pfctx = (const int32_t*)to_device("pfctx.bin", NULL);
+    const int32_t* pfbt = (const int32_t*)to_device("pfbt.bin", NULL);
+    hip_check(hipMalloc(&pfout, pfq_bytes), "hipMalloc pfout");
+    hip_check(hipMalloc((void**)&pflse, (size_t)pf_tokens * hq * sizeof(float)), "hipMalloc pflse");
+    const size_t pws_bytes =
+        pkv_prefill_workspace_bytes(&cache, num_reqs, pf_tokens, hq, max_chunk, max_total, 0);
+    void* pws = NULL;
+    if (pws_bytes > 0) hip_check(hipMalloc(&pws, pws_bytes), "hipMalloc prefill workspace");
+
+    pkv_append_batch ab;
+    memset(&ab, 0, sizeof ab);
+    ab.k_new = knew;
+    ab.v_new = vnew;
+    ab.in_dtype = in_dtype;
+    ab.cu_new_tokens = cu;
+    ab.start_pos = start;
+    ab.block_tables = stepbt;
+    ab.bt_stride = step_stride;
+    ab.num_rows = step_rows;
+    ab.num_new_tokens = step_tokens;
+    pkv_decode_batch db;
+    memset(&db, 0, sizeof db);
+    db.q = q;
+    db.q_dtype = PKV_BF16;
+    db.out = out;
+    db.out_dtype = PKV_BF16;
+    db.lse = lse;
+    db.block_tables = bt;
+    db.bt_stride = bt_stride;
+    db.context_lens = lens;
+    db.num_seqs = seqs;
+    db.num_q_heads = hq;
+    db.max_context_len = max_len;
+    db.split_tokens = 0;
+    db.workspace = ws;
+    db.workspace_bytes = ws_bytes;
+    pkv_prefill_batch pb;
+    memset(&pb, 0, sizeof pb);
+    pb.q = pfq;
+    pb.q_dtype = PKV_BF16;
+    pb.out = pfout;
+    pb.out_dtype = PKV_BF16;
+    pb.lse = pflse;
+    pb.cu_q_lens = pfcu;
+    pb.ctx_before = pfctx;
+    pb.block_tables = pfbt;
+    pb.bt_stride = pf_stride;
+    pb.num_reqs = num_reqs;
+    pb.num_q_tokens = pf_tokens;
+    pb.num_q_heads = hq;
+    pb.max_chunk_len = max_chunk;
+    pb.max_total_len = max_total;
+    pb.split_tokens = 0;
+    pb.workspace = pws;
+    pb.workspace_bytes = pws_bytes;
+    hipStream_t main_stream, side;
+    hip_check(hipStreamCreate(&main_stream), "hipStreamCreate");
+    hip_check(hipStreamCreate(&side), "hipStreamCreate");
+    pkv_check(pkv_mixed_step(&cache, &ab, &db, &pb, sm_scale, main_stream, side),
+              "pkv_mixed_step");
+    hip_check(hipStreamSynchronize(main_stream), "hipStreamSynchronize");
+    printf("decode_client: mixed step, %d prefill requests, %d chunk rows, prefill workspace %zu bytes\n",
+           num_reqs, pf_tokens, pws_bytes);
+  }
   hip_check(hipDeviceSynchronize(), "hipDeviceSynchronize");
 
   from_device("kpool_out.bin", cache.k_pool, pool_bytes);
   from_device("vpool_out.bin", cache.v_pool, pool_bytes);
   from_device("out.bin", out, q_bytes);
   from_device("lse.bin", lse, (size_t)seqs * hq * sizeof(float));
+  if (mixed) {
+    from_device("pfout.bin", pfout, pfq_bytes);
+    from_device("pflse.bin", pflse, (size_t)pf_tokens * hq * sizeof(float));
+  }
   printf("decode_client: workspace %zu bytes, done\n", ws_bytes);
   return 0;
 }

@@ -1,6 +1,7 @@
 """The C ABI on its own: a plain C program (tests/abi_c/decode_client.c,
 built here with gcc against include/pagedkv.h and libpagedkv.so) appends one
-decode step and decodes, in a process with no Python and no PyTorch.  Its
+decode step and decodes, or runs one pkv_mixed_step with chunked prefill on
+a second stream, in a process with no Python and no PyTorch.  Its
 pools must equal the oracle's byte for byte and its outputs must match the
 oracle within the decode tolerances ("TensorRT-LLM框架解析与高性能推理优化实践"
 §4.2 and §6.2: the block-table write and walk; §6.1: the one-pass softmax)."""
@@ -25,10 +26,12 @@ TOL = {"bf16": (2e-2, 2e-3), "fp8": (6e-2, None), "int8": (2e-2, 2e-3)}
 LSE_TOL = 2e-3
 
 CASES = [
-    # lens, Hq, Hkv, D, P, kv
-    ((1, 33, 200, 700, 2100), 16, 4, 128, 32, "bf16"),   # matrix-core decode, several ranges
-    ((5, 64, 65, 900), 8, 8, 128, 64, "bf16"),           # vector decode (MHA)
-    ((1, 129, 1500), 64, 8, 128, 64, "fp8"),             # fp8 codes written from f32 input
+    # lens, Hq, Hkv, D, P, kv, prefill (ctx_before per request, chunk) or None
+    ((1, 33, 200, 700, 2100), 16, 4, 128, 32, "bf16", None),   # matrix-core decode, ranges
+    ((5, 64, 65, 900), 8, 8, 128, 64, "bf16", None),           # vector decode (MHA)
+    ((1, 129, 1500), 64, 8, 128, 64, "fp8", None),             # fp8 codes from f32 input
+    # one pkv_mixed_step call: decode beside chunked prefill on a second stream
+    ((5, 300, 1000), 32, 8, 128, 32, "bf16", ((0, 100, 1800), 200)),
 ]
 
 
@@ -62,6 +65,14 @@ def _write_inputs(d, wl, kp0, vp0):
     if s.kv_dtype in ("fp8", "int8"):
         files["kscale.bin"] = wl.k_scale.astype(np.float32)
         files["vscale.bin"] = wl.v_scale.astype(np.float32)
+    if wl.num_prefill:
+        tot = wl.pf_ctx_before + np.diff(wl.pf_cu)
+        (d / "pfmeta.txt").write_text(" ".join(str(x) for x in (
+            wl.num_prefill, int(wl.pf_cu[-1]), int(np.diff(wl.pf_cu).max()), int(tot.max()),
+            wl.pf_block_tables.shape[1])) + "\n")
+        files.update({"pfq.bin": wl.pf_q, "pfcu.bin": wl.pf_cu.astype(np.int32),
+                      "pfctx.bin": wl.pf_ctx_before.astype(np.int32),
+                      "pfbt.bin": wl.pf_block_tables.astype(np.int32)})
     for name, arr in files.items():
         (d / name).write_bytes(np.ascontiguousarray(arr).tobytes())
 
@@ -71,9 +82,10 @@ def _write_inputs(d, wl, kp0, vp0):
 def test_c_client_append_and_decode_match_oracle(case, tmp_path):
     if shutil.which("gcc") is None:
         pytest.fail("gcc is needed to build the C client")
-    lens, hq, hkv, hd, page, kv = case
+    lens, hq, hkv, hd, page, kv, pf = case
+    extra = dict(prefill_ctx=pf[0], prefill_chunk=pf[1]) if pf else {}
     spec = wk.custom_spec(lens, num_q_heads=hq, num_kv_heads=hkv, head_dim=hd, page_size=page,
-                          q_dtype="bf16", kv_dtype=kv, out_dtype="bf16")
+                          q_dtype="bf16", kv_dtype=kv, out_dtype="bf16", **extra)
     wl = wk.make_workload(spec, seed=77)
     kp0, vp0 = sup.oracle_pools(wl, with_step=False)
     kp1, vp1 = sup.oracle_pools(wl, with_step=True)
@@ -102,3 +114,13 @@ def test_c_client_append_and_decode_match_oracle(case, tmp_path):
     lse = np.frombuffer((d / "lse.bin").read_bytes(), dtype=np.float32).reshape(ref_lse.shape)
     assert np.abs(lse.astype(np.float64) - ref_lse).max() <= LSE_TOL
     print(f"[c-client] max |err| {err.max():.3g}, mean {err.mean():.3g}", flush=True)
+    if pf:
+        pref, plse = sup.oracle_prefill(wl, kp1, vp1)
+        pout = np.frombuffer((d / "pfout.bin").read_bytes(), dtype=np.uint16).reshape(pref.shape)
+        pg = sup.to_f64(pout, "bf16")
+        perr = np.abs(pg - pref)
+        assert np.isfinite(pg).all()
+        assert perr.max() <= mx and perr.mean() <= mean_bar, (perr.max(), perr.mean())
+        pl = np.frombuffer((d / "pflse.bin").read_bytes(), dtype=np.float32).reshape(plse.shape)
+        assert np.abs(pl.astype(np.float64) - plse).max() <= LSE_TOL
+        print(f"[c-client] prefill max |err| {perr.max():.3g}, mean {perr.mean():.3g}", flush=True)
