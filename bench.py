@@ -252,9 +252,12 @@ def measure(spec, args, warmup, split_tokens: int, prefill_split: int):
     print(f"[bench] uploaded, split_tokens={dw.split_tokens}", file=sys.stderr, flush=True)
 
     side = torch.cuda.Stream() if args.launch.endswith("mixed_step") else None
+    fused = args.launch == "decode_step"
     for _ in range(warmup):
         if side is not None:
             dw.mixed_step(side_stream=side)
+        elif fused:
+            dw.decode_step()
         else:
             dw.step()
     torch.cuda.synchronize()
@@ -273,6 +276,9 @@ def measure(spec, args, warmup, split_tokens: int, prefill_split: int):
             continue
         if side is not None:
             dw.mixed_step(side_stream=side)
+            continue
+        if fused:
+            dw.decode_step()
             continue
         dw.append_step()
         if wl.num_seqs:
@@ -328,6 +334,8 @@ def measure(spec, args, warmup, split_tokens: int, prefill_split: int):
             graph.replay()
         elif side is not None:
             dw.mixed_step(side_stream=side)
+        elif fused:
+            dw.decode_step()
         else:
             dw.step()
         b.record()
@@ -425,11 +433,14 @@ def main() -> int:
     ap.add_argument("--no-secondary", action="store_true",
                     help="default workload only: skip the 70B-shaped fp8 decode timed beside it")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--launch", choices=("mixed_step", "calls", "graph", "graph_mixed_step"),
+    ap.add_argument("--launch", choices=("mixed_step", "calls", "graph", "graph_mixed_step",
+                                         "decode_step"),
                     default="mixed_step",
                     help="mixed_step: one pkv_mixed_step call per step, prefill on a second "
                          "stream; calls: append, decode and prefill calls one after another; "
-                         "graph / graph_mixed_step: replays of those captured as a HIP graph")
+                         "graph / graph_mixed_step: replays of those captured as a HIP graph; "
+                         "decode_step: one pkv_decode_step call (the append inside the "
+                         "attention launch; decode-only workloads)")
     ap.add_argument("--chunk-sweep", action="store_true",
                     help="instead of the step benchmark: chunked prefill of long prompts at "
                          "several chunk sizes against one context-attention call")

@@ -270,6 +270,48 @@ pkv_status pkv_lse_merge(const pkv_cache_desc* cache, void* out, int32_t out_dty
                          const void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ *
+ * decode_step — one generation step of a decode batch in one attention
+ * launch: every sequence's newest token is written into its page slot and
+ * the sequence's query attends its whole context, that token included.
+ * Each step of in-flight batching places the new token's K/V as the request
+ * grows ("TensorRT-LLM内核融合与动态批处理", In-flight Batching section;
+ * "TensorRT-LLM框架解析与高性能推理优化实践" §4.2 and §6.2 for the block-table
+ * write and walk), and joining the write to the attention kernel removes a
+ * launch per step (Kernel Fusion section of "TensorRT-LLM内核融合与动态批处理";
+ * layer-fusion paragraph of "TensorRT-LLM性能调优：提升LLM推理效率" on the
+ * cost of each launch).
+ *
+ * Equivalent, bit for bit in pools, out and lse, to
+ *   pkv_kv_cache_append(k_new, v_new, cu = {0, 1, .., num_seqs},
+ *                       start_pos[s] = context_lens[s] - 1)
+ * followed by pkv_paged_attn_decode with the remaining arguments, for
+ * sequences with context_lens[s] >= 1; a sequence with context_lens[s] = 0
+ * appends nothing and gets out = 0, lse = -inf.
+ *
+ * k_new, v_new : device [num_seqs][num_kv_heads][head_dim], the new token of
+ *                each sequence (position context_lens[s] - 1 of block-table
+ *                row s); in_dtype and the stored encoding as for
+ *                pkv_kv_cache_append.  Row s is read only if
+ *                context_lens[s] >= 1.
+ * The remaining arguments, the supported dtypes, split_tokens, the
+ * workspace and its size are those of pkv_paged_attn_decode.  The page that
+ * receives a sequence's new token must not be shared with another sequence
+ * of the call.
+ * Errors: the checks of pkv_paged_attn_decode; in_dtype other than the
+ * append's (PKV_ERR_UNSUPPORTED); k_new or v_new NULL with num_seqs > 0
+ * (PKV_ERR_INVALID_ARG).  Nothing is launched on error.
+ * ------------------------------------------------------------------------ */
+pkv_status pkv_decode_step(const pkv_cache_desc* cache,
+                           const void* k_new, const void* v_new, int32_t in_dtype,
+                           const void* q, int32_t q_dtype,
+                           void* out, int32_t out_dtype, float* lse,
+                           const int32_t* block_tables, int32_t bt_stride,
+                           const int32_t* context_lens, int32_t num_seqs,
+                           int32_t num_q_heads, int32_t max_context_len,
+                           float sm_scale, int32_t split_tokens,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ *
  * paged_attn_decode_noalloc — pkv_paged_attn_decode for callers that cannot
  * allocate device memory (code under stream capture, tight serving loops,
  * harnesses that forbid allocation): the same kernels and results, with the

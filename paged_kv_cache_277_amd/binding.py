@@ -109,6 +109,8 @@ _SIGS = {
     "pkv_decode_split_tokens": (_I, [_P, _I, _I, _I]),
     "pkv_decode_workspace_bytes": (_SZ, [_P, _I, _I, _I, _I]),
     "pkv_paged_attn_decode": (_I, [_P, _P, _I, _P, _I, _P, _P, _I, _P, _I, _I, _I, _F, _I, _P, _SZ, _P]),
+    "pkv_decode_step": (_I, [_P, _P, _P, _I, _P, _I, _P, _I, _P, _P, _I, _P, _I, _I, _I, _F, _I,
+                             _P, _SZ, _P]),
     "pkv_paged_attn_decode_noalloc": (_I, [_P, _P, _I, _P, _I, _P, _P, _I, _P, _I, _I, _I, _F, _I, _P]),
     "pkv_paged_attn_decode_partial": (_I, [_P, _P, _I, _P, _I, _P, _P, _I, _P, _I, _I, _I, _F, _I, _P, _SZ, _P]),
     "pkv_paged_attn_decode_partial_listed": (_I, [_P, _P, _I, _P, _I, _P, _P, _I, _P, _I, _I, _I, _F, _I, _P, _SZ, _P]),
@@ -426,6 +428,45 @@ def pkv_paged_attn_decode(cache: PagedCache, q: torch.Tensor, out: torch.Tensor,
                                        _ptr(lse), _ptr(block_tables), block_tables.shape[1],
                                        _ptr(context_lens), q.shape[0], q.shape[1], max_context_len,
                                        float(sm_scale), split_tokens, wp, wb, _stream(stream)))
+
+
+class DecodeStepCall:
+    """pkv_decode_step with its arguments checked and marshalled once; each
+    call issues the C call alone (for launch-bound step loops).  It holds the
+    tensors, so their memory stays allocated while it lives."""
+
+    def __init__(self, cache: PagedCache, k_new: torch.Tensor, v_new: torch.Tensor,
+                 q: torch.Tensor, out: torch.Tensor, block_tables: torch.Tensor,
+                 context_lens: torch.Tensor, max_context_len: int, sm_scale: float,
+                 lse: Optional[torch.Tensor] = None, split_tokens: int = 0,
+                 workspace: Optional[torch.Tensor] = None):
+        _decode_args(cache, q, out, lse, block_tables, context_lens)
+        _need(k_new.shape == v_new.shape and k_new.dim() == 3, "k_new/v_new must be [B][Hkv][D]")
+        _need(k_new.is_contiguous() and v_new.is_contiguous(), "k_new/v_new must be contiguous")
+        _need(k_new.shape == (q.shape[0], cache.num_kv_heads, cache.head_dim),
+              "k_new shape mismatch")
+        wp, wb = _ws(workspace)
+        self._fn = lib().pkv_decode_step
+        self._args = (cache.desc, _ptr(k_new), _ptr(v_new), _code_of(k_new), _ptr(q),
+                      _code_of(q), _ptr(out), _code_of(out), _ptr(lse), _ptr(block_tables),
+                      block_tables.shape[1], _ptr(context_lens), q.shape[0], q.shape[1],
+                      max_context_len, float(sm_scale), split_tokens, wp, wb)
+        self._tensors = (cache, k_new, v_new, q, out, lse, block_tables, context_lens, workspace)
+
+    def __call__(self, stream=None) -> None:
+        _check(self._fn(*self._args, _stream(stream)))
+
+
+def pkv_decode_step(cache: PagedCache, k_new: torch.Tensor, v_new: torch.Tensor,
+                    q: torch.Tensor, out: torch.Tensor, block_tables: torch.Tensor,
+                    context_lens: torch.Tensor, max_context_len: int, sm_scale: float,
+                    lse: Optional[torch.Tensor] = None, split_tokens: int = 0,
+                    workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """One decode step in one attention launch: sequence s's new token
+    (k_new[s], v_new[s], [B][Hkv][D]) is written at position
+    context_lens[s] - 1, then the sequence's query attends its context."""
+    DecodeStepCall(cache, k_new, v_new, q, out, block_tables, context_lens, max_context_len,
+                   sm_scale, lse, split_tokens, workspace)(stream)
 
 
 NOALLOC_SCRATCH_BYTES = 32 << 20      # PKV_NOALLOC_SCRATCH_BYTES of include/pagedkv.h

@@ -430,6 +430,17 @@ pkv_status prepare_prefill(const pkv_cache_desc* cache, int32_t q_dtype, int32_t
   return PKV_OK;
 }
 
+// New K/V rows come in the cache's own dtype for F32/BF16 caches and as
+// float32 for 8-bit caches (encoded on the way in).
+pkv_status check_append_input(const pkv_cache_desc* cache, int32_t in_dtype) {
+  const int32_t want_in =
+      (cache->kv_dtype == PKV_FP8_E4M3FN || cache->kv_dtype == PKV_INT8) ? PKV_F32 : cache->kv_dtype;
+  if (in_dtype != want_in)
+    return fail(PKV_ERR_UNSUPPORTED, "append into kv_dtype %d takes in_dtype %d, got %d",
+                cache->kv_dtype, want_in, in_dtype);
+  return PKV_OK;
+}
+
 pkv_status prepare_append(const pkv_cache_desc* cache, const void* k_new, const void* v_new,
                           int32_t in_dtype, const int32_t* cu_new_tokens,
                           const int32_t* start_pos, const int32_t* block_tables,
@@ -437,11 +448,7 @@ pkv_status prepare_append(const pkv_cache_desc* cache, const void* k_new, const 
                           pkv::AppendArgs* a) {
   pkv_status st;
   if ((st = check_cache(cache)) != PKV_OK) return st;
-  const int32_t want_in =
-      (cache->kv_dtype == PKV_FP8_E4M3FN || cache->kv_dtype == PKV_INT8) ? PKV_F32 : cache->kv_dtype;
-  if (in_dtype != want_in)
-    return fail(PKV_ERR_UNSUPPORTED, "append into kv_dtype %d takes in_dtype %d, got %d",
-                cache->kv_dtype, want_in, in_dtype);
+  if ((st = check_append_input(cache, in_dtype)) != PKV_OK) return st;
   if (num_rows < 0 || num_new_tokens < 0)
     return fail(PKV_ERR_INVALID_ARG, "num_rows %d / num_new_tokens %d negative", num_rows,
                 num_new_tokens);
@@ -677,6 +684,26 @@ pkv_status pkv_paged_attn_decode(const pkv_cache_desc* cache, const void* q, int
                                  context_lens, num_seqs, num_q_heads, max_context_len, sm_scale,
                                  split_tokens, workspace, workspace_bytes_in, true, &a);
   if (st != PKV_OK) return st;
+  return launch_decode_call(a, static_cast<hipStream_t>(stream));
+}
+
+pkv_status pkv_decode_step(const pkv_cache_desc* cache, const void* k_new, const void* v_new,
+                           int32_t in_dtype, const void* q, int32_t q_dtype, void* out,
+                           int32_t out_dtype, float* lse, const int32_t* block_tables,
+                           int32_t bt_stride, const int32_t* context_lens, int32_t num_seqs,
+                           int32_t num_q_heads, int32_t max_context_len, float sm_scale,
+                           int32_t split_tokens, void* workspace, size_t workspace_bytes_in,
+                           void* stream) {
+  pkv::AttnArgs a;
+  pkv_status st = prepare_decode(cache, q, q_dtype, out, out_dtype, lse, block_tables, bt_stride,
+                                 context_lens, num_seqs, num_q_heads, max_context_len, sm_scale,
+                                 split_tokens, workspace, workspace_bytes_in, true, &a);
+  if (st != PKV_OK) return st;
+  if ((st = check_append_input(cache, in_dtype)) != PKV_OK) return st;
+  if (num_seqs > 0 && (!k_new || !v_new))
+    return fail(PKV_ERR_INVALID_ARG, "k_new / v_new must not be NULL");
+  a.new_k = k_new;
+  a.new_v = v_new;
   return launch_decode_call(a, static_cast<hipStream_t>(stream));
 }
 

@@ -11,6 +11,7 @@
 // Hkv x head_dim row in 16-byte output pieces, so every page row is written
 // with full 16-byte stores and the packed input is read contiguously.
 #include "decode_list.h"
+#include "kv_write.h"
 #include "pkv_device.h"
 #include "pkv_launch.h"
 
@@ -19,8 +20,7 @@ namespace {
 
 template <int KVT>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
-  constexpr int KVB = KvBytes<KVT>::value;
-  constexpr int EPL = 16 / KVB;                  // cache elements per 16-byte piece
+  constexpr int EPL = 16 / KvBytes<KVT>::value;  // cache elements per 16-byte piece
   if (a.list.list && blockIdx.x == a.num_tokens) {   // the extra workgroup: decode work list
     build_decode_list(a.list);
     return;
@@ -34,38 +34,10 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   const int D = a.c.head_dim, Hkv = a.c.num_kv_heads;
   const int pieces = D / EPL;                    // per head
   const int total = Hkv * pieces;
-  uint8_t* kdst = static_cast<uint8_t*>(a.c.k_pool_w);
-  uint8_t* vdst = static_cast<uint8_t*>(a.c.v_pool_w);
   for (int c = threadIdx.x; c < total; c += blockDim.x) {
     const int j = c / pieces, pc = c % pieces;
-    const size_t dst = ((((size_t)page * Hkv + j) * P + slot) * D + (size_t)pc * EPL) * KVB;
     const size_t src_e = ((size_t)t * Hkv + j) * D + (size_t)pc * EPL;   // input element
-    if constexpr (KvCoded<KVT>::value) {
-      // F32 input: 16 floats -> 16 codes (fp8 or int8).
-      const float ks = a.c.k_scale[j], vs = a.c.v_scale[j];
-      const u32x4* ksrc = reinterpret_cast<const u32x4*>(static_cast<const float*>(a.k_new) + src_e);
-      const u32x4* vsrc = reinterpret_cast<const u32x4*>(static_cast<const float*>(a.v_new) + src_e);
-      u32x4 ko, vo;
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const u32x4 kx = ksrc[q4], vx = vsrc[q4];
-        uint32_t kw = 0, vw = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          kw |= f32_to_code<KVT>(__uint_as_float(kx[e]) / ks) << (8 * e);
-          vw |= f32_to_code<KVT>(__uint_as_float(vx[e]) / vs) << (8 * e);
-        }
-        ko[q4] = kw;
-        vo[q4] = vw;
-      }
-      *reinterpret_cast<u32x4*>(kdst + dst) = ko;
-      *reinterpret_cast<u32x4*>(vdst + dst) = vo;
-    } else {
-      const uint8_t* ks = static_cast<const uint8_t*>(a.k_new) + src_e * KVB;
-      const uint8_t* vs = static_cast<const uint8_t*>(a.v_new) + src_e * KVB;
-      *reinterpret_cast<u32x4*>(kdst + dst) = ld16(ks);
-      *reinterpret_cast<u32x4*>(vdst + dst) = ld16(vs);
-    }
+    write_kv_piece<KVT>(a.c, a.k_new, a.v_new, src_e, kv_piece_offset<KVT>(a.c, page, j, slot, pc), j);
   }
 }
 

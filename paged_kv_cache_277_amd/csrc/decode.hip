@@ -23,6 +23,11 @@
 // Output of a work item: if the row needs one range, the final output and
 // log-sum-exp; otherwise (m, l, acc) into the workspace for the merge.
 // m is kept in the log2 domain (scores are pre-multiplied by log2(e)).
+//
+// Both decode kernels (this one and decode_mfma.hip) also come in a fused
+// step form (STEP = true, pkv_decode_step): the range that ends at a
+// sequence's new token first stores that token's K/V row (kv_write.h), one
+// 16-byte piece from each lane that later loads it.
 #include <math.h>
 
 #include <algorithm>
@@ -30,6 +35,7 @@
 #include <type_traits>
 
 #include "decode_list.h"
+#include "kv_write.h"
 #include "pkv_device.h"
 #include "pkv_launch.h"
 
@@ -124,7 +130,7 @@ __device__ __forceinline__ void load_q_slice(const void* q, size_t idx, float mu
   }
 }
 
-template <int KVT, int D, int GMAX>
+template <int KVT, int D, int GMAX, bool STEP>
 __global__ __launch_bounds__(256) void decode_partial_vec(AttnArgs a) {
   using S = VecShape<KVT, D>;
   using QT = typename std::conditional<KVT == KV_F32, float, uint16_t>::type;
@@ -175,6 +181,18 @@ __global__ __launch_bounds__(256) void decode_partial_vec(AttnArgs a) {
   const int lane = threadIdx.x & 63;
   const int w = uniform(threadIdx.x >> 6);
   const int rg = lane / R, col = lane % R;
+  // Fused decode step: the range that ends at the new token (position
+  // L - 1) stores it.  Its tile (TOK tokens) belongs to wave
+  // (o / TOK) % kWaves, which loads row o % TOK of the tile with the lanes
+  // of row group (o % TOK) % RW, lane col taking piece col; those lanes
+  // store exactly the pieces they load later.
+  [[maybe_unused]] bool step_lane = false;
+  [[maybe_unused]] StepPiece<KVT> step_piece;
+  if constexpr (STEP) {
+    const int o = L - 1 - t_begin;
+    step_lane = t_end == L && w == (o / TOK) % kWaves && rg == (o % TOK) % RW;
+    if (step_lane) step_piece.load(a, z, j, L - 1, col);
+  }
 
   float kscale = 1.0f, vscale = 1.0f;
   if constexpr (KvCoded<KVT>::value) { kscale = a.c.k_scale[j]; vscale = a.c.v_scale[j]; }
@@ -291,6 +309,9 @@ __global__ __launch_bounds__(256) void decode_partial_vec(AttnArgs a) {
   const int ta = tw0 < t_end ? tw0 : ((t_end - 1) & ~(TOK - 1));
   const int pg0 = btrow[ta >> pshift];
   int pg_next = page_of(1);
+  if constexpr (STEP) {
+    if (step_lane) step_piece.store(a);
+  }
   load(kA, vA, pg0, ta);
   // step(k): page id of tile k+2, loads of tile k+1 into nxt, score tile k.
   auto step = [&](int k, const u32x4 (&kc)[U], const u32x4 (&vc)[U], u32x4 (&kn)[U],
@@ -376,21 +397,25 @@ __global__ __launch_bounds__(256) void decode_list_kernel(DecodeListArgs a) {
   build_decode_list(a);
 }
 
-template <int KVT, int D>
+template <int KVT, int D, bool STEP>
 hipError_t launch_vec_d(const AttnArgs& a, dim3 grid, hipStream_t s) {
   const int G = a.num_q_heads / a.c.num_kv_heads;
   const dim3 block(256);
-  if (G <= 1) hipLaunchKernelGGL((decode_partial_vec<KVT, D, 1>), grid, block, 0, s, a);
-  else if (G <= 2) hipLaunchKernelGGL((decode_partial_vec<KVT, D, 2>), grid, block, 0, s, a);
-  else if (G <= 4) hipLaunchKernelGGL((decode_partial_vec<KVT, D, 4>), grid, block, 0, s, a);
-  else if (G <= 8) hipLaunchKernelGGL((decode_partial_vec<KVT, D, 8>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((decode_partial_vec<KVT, D, 16>), grid, block, 0, s, a);
+  if (G <= 1) hipLaunchKernelGGL((decode_partial_vec<KVT, D, 1, STEP>), grid, block, 0, s, a);
+  else if (G <= 2) hipLaunchKernelGGL((decode_partial_vec<KVT, D, 2, STEP>), grid, block, 0, s, a);
+  else if (G <= 4) hipLaunchKernelGGL((decode_partial_vec<KVT, D, 4, STEP>), grid, block, 0, s, a);
+  else if (G <= 8) hipLaunchKernelGGL((decode_partial_vec<KVT, D, 8, STEP>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((decode_partial_vec<KVT, D, 16, STEP>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
 template <int KVT>
 hipError_t launch_vec(const AttnArgs& a, dim3 grid, hipStream_t s) {
-  return a.c.head_dim == 64 ? launch_vec_d<KVT, 64>(a, grid, s) : launch_vec_d<KVT, 128>(a, grid, s);
+  if (a.new_k)
+    return a.c.head_dim == 64 ? launch_vec_d<KVT, 64, true>(a, grid, s)
+                              : launch_vec_d<KVT, 128, true>(a, grid, s);
+  return a.c.head_dim == 64 ? launch_vec_d<KVT, 64, false>(a, grid, s)
+                            : launch_vec_d<KVT, 128, false>(a, grid, s);
 }
 
 hipError_t launch_vec_any(const AttnArgs& a, dim3 grid, hipStream_t s) {

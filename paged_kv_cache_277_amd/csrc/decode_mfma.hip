@@ -36,11 +36,13 @@
 // Work decomposition: like the vector path, one workgroup of 4 waves per
 // (row, KV head, context range); each wave walks 32-token tiles of the range
 // with its own softmax state, the next tile's K/V loads in flight while the
-// current tile is computed.  Scores are kept in the log2 domain.
+// current tile is computed.  Scores are kept in the log2 domain.  The
+// fused step form (STEP = true) is described in decode.hip.
 #include <math.h>
 
 #include <type_traits>
 
+#include "kv_write.h"
 #include "pkv_device.h"
 #include "pkv_launch.h"
 
@@ -127,7 +129,7 @@ __device__ __forceinline__ void load_tile(TileRegs<KVT, D>& r, const uint8_t* kp
   }
 }
 
-template <int KVT, int D>
+template <int KVT, int D, bool STEP>
 __global__ __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(KvBytes<KVT>::value == 1 || D == 64 ? 3 : 2)))
 void decode_partial_mfma(AttnArgs a) {
@@ -191,6 +193,18 @@ void decode_partial_mfma(AttnArgs a) {
   uint8_t* lds = smem + w * kTile * LDS_ROW;
   constexpr int STRIDE = kWaves * kTile;
   const uint32_t loff = (uint32_t)((lane / R) * ROWB + (lane % R) * 16);
+  // Fused decode step: the range that ends at the new token (position
+  // L - 1) stores it.  Its tile belongs to wave (o / kTile) % kWaves, which
+  // loads row b = o % 16 of the token's 16-token block with the lanes
+  // l / R = b % RPI, lane l taking piece l % R (load_tile); those lanes
+  // store exactly the pieces they load later.
+  [[maybe_unused]] bool step_lane = false;
+  [[maybe_unused]] StepPiece<KVT> step_piece;
+  if constexpr (STEP) {
+    const int o = L - 1 - t_begin;
+    step_lane = t_end == L && w == (o / kTile) % kWaves && lane / R == (o & 15) % RPI;
+    if (step_lane) step_piece.load(a, z, j, L - 1, lane % R);
+  }
   // This wave's tiles are t_begin + w*kTile + k*STRIDE, k = 0..nt-1.
   const int tw0 = t_begin + w * kTile;
   const int nt = tw0 < t_end ? (t_end - tw0 + STRIDE - 1) / STRIDE : 0;
@@ -233,6 +247,9 @@ void decode_partial_mfma(AttnArgs a) {
   // Only a range's last tile can hold tokens past its end, so every tile of
   // the main loop is computed without masks.
   TR buf0, buf1;
+  if constexpr (STEP) {
+    if (step_lane) step_piece.store(a);
+  }
   load_tile<KVT, D>(buf0, kp, vp, pn0, pn1, ta, t_end, Hkv, j, pshift, loff);
   pn0 = pq0;                                    // pages of the next tile to load
   pn1 = pq1;
@@ -445,19 +462,27 @@ bool decode_mfma_supported(const AttnArgs& a) {
          (a.split_tokens >> a.page_shift) + 2 <= kMaxRangePages;
 }
 
-hipError_t launch_decode_partial_mfma(const AttnArgs& a, hipStream_t s) {
-  const dim3 grid = a.plan ? decode_plan_grid(a) : dim3(a.c.num_kv_heads, a.num_rows, a.max_splits);
+namespace {
+template <bool STEP>
+void launch_mfma_step(const AttnArgs& a, dim3 grid, hipStream_t s) {
   const dim3 block(256);
   if (a.c.kv_dtype == KV_BF16) {
-    if (a.c.head_dim == 128) hipLaunchKernelGGL((decode_partial_mfma<KV_BF16, 128>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((decode_partial_mfma<KV_BF16, 64>), grid, block, 0, s, a);
+    if (a.c.head_dim == 128) hipLaunchKernelGGL((decode_partial_mfma<KV_BF16, 128, STEP>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((decode_partial_mfma<KV_BF16, 64, STEP>), grid, block, 0, s, a);
   } else if (a.c.kv_dtype == KV_FP8) {
-    if (a.c.head_dim == 128) hipLaunchKernelGGL((decode_partial_mfma<KV_FP8, 128>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((decode_partial_mfma<KV_FP8, 64>), grid, block, 0, s, a);
+    if (a.c.head_dim == 128) hipLaunchKernelGGL((decode_partial_mfma<KV_FP8, 128, STEP>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((decode_partial_mfma<KV_FP8, 64, STEP>), grid, block, 0, s, a);
   } else {
-    if (a.c.head_dim == 128) hipLaunchKernelGGL((decode_partial_mfma<KV_INT8, 128>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((decode_partial_mfma<KV_INT8, 64>), grid, block, 0, s, a);
+    if (a.c.head_dim == 128) hipLaunchKernelGGL((decode_partial_mfma<KV_INT8, 128, STEP>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((decode_partial_mfma<KV_INT8, 64, STEP>), grid, block, 0, s, a);
   }
+}
+}  // namespace
+
+hipError_t launch_decode_partial_mfma(const AttnArgs& a, hipStream_t s) {
+  const dim3 grid = a.plan ? decode_plan_grid(a) : dim3(a.c.num_kv_heads, a.num_rows, a.max_splits);
+  if (a.new_k) launch_mfma_step<true>(a, grid, s);
+  else launch_mfma_step<false>(a, grid, s);
   return hipGetLastError();
 }
 

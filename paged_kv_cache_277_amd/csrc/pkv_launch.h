@@ -64,6 +64,10 @@ struct AttnArgs {
   int32_t prefill;
   int32_t contiguous;            // prefill over contiguous K/V [tokens][Hkv][D] (no pages)
   int32_t page_shift;            // log2(page_size)
+  // fused decode step: each sequence's new token (position L - 1), packed
+  // [num_seqs][Hkv][D], written by the decode launch itself; null otherwise
+  const void* new_k;
+  const void* new_v;
 };
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);

@@ -16,7 +16,7 @@ import numpy as np
 import torch
 
 from . import binding as B
-from .workloads import POISON, Workload
+from .workloads import POISON, Workload, decode_step_tokens
 
 _TORCH_STORAGE = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8,
                   "int8": torch.int8}
@@ -78,6 +78,7 @@ class DeviceWorkload:
     workspace: Optional[torch.Tensor]
     pf: dict = field(default_factory=dict)
     _batches: Optional[tuple] = None
+    _step_call: Optional[B.DecodeStepCall] = None
 
     def setup(self, stream=None) -> None:
         self._append(self.setup_batch, stream)
@@ -97,6 +98,23 @@ class DeviceWorkload:
                                 float(self.wl.sm_scale), lse=self.lse,
                                 split_tokens=self.split_tokens, workspace=self.workspace,
                                 stream=stream)
+
+    def decode_step(self, stream=None) -> None:
+        """Append every sequence's step token and decode in one attention
+        launch (pkv_decode_step).  Decode-only workloads whose sequences each
+        append a token of their own."""
+        if self.wl.num_seqs == 0:
+            return
+        if self._step_call is None:
+            if self.pf:
+                raise ValueError("decode_step: the workload has a prefill part")
+            kn, vn = decode_step_tokens(self.wl)
+            d, dt = self.q.device, self.wl.spec.kv_in_dtype
+            self._step_call = B.DecodeStepCall(
+                self.cache, _dev(kn, dt, d), _dev(vn, dt, d), self.q, self.out, self.bt,
+                self.lens, self.max_len, float(self.wl.sm_scale), lse=self.lse,
+                split_tokens=self.split_tokens, workspace=self.workspace)
+        self._step_call(stream)
 
     def decode_partial(self, stream=None, listed: bool = False) -> None:
         """The partial pass; listed=True takes its items from the work list

@@ -421,6 +421,28 @@ def logical_kv(wl: Workload, kind: str, idx: int, length: int) -> Tuple[np.ndarr
     return k, v
 
 
+def decode_step_tokens(wl: Workload) -> Tuple[np.ndarray, np.ndarray]:
+    """The step's decode tokens as one row per sequence, [B][Hkv][D] in the
+    input dtype: row b is the step-batch token that goes to position L_b - 1
+    of sequence b (zero rows for empty sequences).  Raises ValueError when a
+    non-empty sequence has no token of its own in the step (its last
+    position lies in a shared prefix)."""
+    st, s = wl.step, wl.spec
+    k = np.zeros((wl.num_seqs, s.num_kv_heads, s.head_dim), st.k.dtype)
+    v = np.zeros_like(k)
+    have = np.zeros(wl.num_seqs, bool)
+    for i, o in enumerate(st.owners):
+        if o[0] != "seq":
+            continue
+        b = o[1]
+        if st.cu[i + 1] - st.cu[i] != 1 or st.start_pos[i] != wl.context_lens[b] - 1:
+            raise ValueError(f"step row {i} is not sequence {b}'s last token")
+        k[b], v[b], have[b] = st.k[st.cu[i]], st.v[st.cu[i]], True
+    if not np.array_equal(have, wl.context_lens > 0):
+        raise ValueError("some sequences end inside a shared prefix: no token of their own")
+    return k, v
+
+
 def custom_spec(lens: Sequence[int], *, num_q_heads: int, num_kv_heads: int, head_dim: int,
                 page_size: int, q_dtype: str = "bf16", kv_dtype: str = "bf16",
                 out_dtype: Optional[str] = None, shared_prefix_pages: int = 0,

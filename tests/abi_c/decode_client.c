@@ -15,6 +15,10 @@
  *   q.bin bt.bin lens.bin         decode query (bf16), block tables, lengths
  * Outputs: kpool_out.bin vpool_out.bin out.bin (bf16) lse.bin (float).
  *
+ * With a file fused.txt beside them, knew.bin / vnew.bin hold one row per
+ * sequence ([num_seqs][num_kv_heads][head_dim], the token at position
+ * L - 1) and one pkv_decode_step call replaces the append and the decode.
+ *
  * With a file pfmeta.txt (num_reqs num_q_tokens max_chunk_len max_total_len
  * pf_bt_stride) and pfq.bin pfcu.bin pfctx.bin pfbt.bin beside them, the
  * three parts (append, decode, chunked prefill) run instead as one
@@ -153,11 +157,17 @@ int main(int argc, char** argv) {
   if (ws_bytes > 0) hip_check(hipMalloc(&ws, ws_bytes), "hipMalloc workspace");
 
   const int mixed = exists("pfmeta.txt");
+  const int fused = exists("fused.txt");
   void* pfout = NULL;
   float* pflse = NULL;
   size_t pfq_bytes = 0;
   int num_reqs = 0, pf_tokens = 0;
-  if (!mixed) {
+  if (fused) {
+    pkv_check(pkv_decode_step(&cache, knew, vnew, in_dtype, q, PKV_BF16, out, PKV_BF16, lse, bt,
+                              bt_stride, lens, seqs, hq, max_len, sm_scale, 0, ws, ws_bytes, NULL),
+              "pkv_decode_step");
+    printf("decode_client: fused decode step\n");
+  } else if (!mixed) {
     pkv_check(pkv_kv_cache_append(&cache, knew, vnew, in_dtype, cu, start, stepbt, step_stride,
                                   step_rows, step_tokens, NULL),
               "pkv_kv_cache_append");

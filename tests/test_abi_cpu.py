@@ -161,6 +161,37 @@ def test_decode_rejects_bad_arguments():
     assert _decode(i8, out_dtype=B.PKV_F32) == B.PKV_ERR_UNSUPPORTED
 
 
+def _step(desc, in_dtype=B.PKV_BF16, k_new=FAKE, v_new=FAKE, B_=2, **kw):
+    a = dict(q_dtype=B.PKV_BF16, out_dtype=B.PKV_BF16, Hq=4, max_len=64, stride=4, split=0,
+             ws=None, wsb=0, scale=0.125)
+    a.update(kw)
+    return B.lib().pkv_decode_step(C.byref(desc), k_new, v_new, in_dtype, FAKE, a["q_dtype"], FAKE,
+                                   a["out_dtype"], None, FAKE, a["stride"], FAKE, B_, a["Hq"],
+                                   a["max_len"], a["scale"], a["split"], a["ws"], a["wsb"], None)
+
+
+@fake_ptrs
+def test_decode_step_rejects_on_host():
+    """The fused step makes every check of the decode call and of the append
+    input before it launches."""
+    d = _desc()
+    assert _step(d, in_dtype=B.PKV_F32) == B.PKV_ERR_UNSUPPORTED    # bf16 cache takes bf16 rows
+    assert _step(d, k_new=None) == B.PKV_ERR_INVALID_ARG
+    assert _step(d, v_new=None) == B.PKV_ERR_INVALID_ARG
+    assert _step(d, Hq=3) == B.PKV_ERR_INVALID_ARG
+    assert _step(d, max_len=65) == B.PKV_ERR_INVALID_ARG
+    assert _step(d, split=32) == B.PKV_ERR_INVALID_ARG                # partials need a workspace
+    assert b"workspace" in B.lib().pkv_last_error()
+    assert _step(d, scale=0.0) == B.PKV_ERR_INVALID_ARG
+    f8 = _desc(kv_dtype=B.PKV_FP8_E4M3FN, k_scale=FAKE, v_scale=FAKE)
+    assert _step(f8, in_dtype=B.PKV_BF16) == B.PKV_ERR_UNSUPPORTED   # 8-bit caches take f32 rows
+    i8 = _desc(kv_dtype=B.PKV_INT8, k_scale=FAKE, v_scale=FAKE)
+    assert _step(i8, in_dtype=B.PKV_INT8) == B.PKV_ERR_UNSUPPORTED
+    assert _step(_desc(head_dim=96)) == B.PKV_ERR_UNSUPPORTED
+    # an empty batch is valid and launches nothing
+    assert _step(d, k_new=None, v_new=None, B_=0) == B.PKV_OK
+
+
 def test_work_list_rejections():
     """pkv_decode_work_list checks its shape arguments like a decode call
     (no GPU needed: every case fails before anything is launched)."""

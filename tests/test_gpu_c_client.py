@@ -1,7 +1,8 @@
 """The C ABI on its own: a plain C program (tests/abi_c/decode_client.c,
 built here with gcc against include/pagedkv.h and libpagedkv.so) appends one
-decode step and decodes, or runs one pkv_mixed_step with chunked prefill on
-a second stream, in a process with no Python and no PyTorch.  Its
+decode step and decodes, runs the same step as one pkv_decode_step call, or
+runs one pkv_mixed_step with chunked prefill on a second stream, in a
+process with no Python and no PyTorch.  Its
 pools must equal the oracle's byte for byte and its outputs must match the
 oracle within the decode tolerances ("TensorRT-LLM框架解析与高性能推理优化实践"
 §4.2 and §6.2: the block-table write and walk; §6.1: the one-pass softmax)."""
@@ -26,12 +27,17 @@ TOL = {"bf16": (2e-2, 2e-3), "fp8": (6e-2, None), "int8": (2e-2, 2e-3)}
 LSE_TOL = 2e-3
 
 CASES = [
-    # lens, Hq, Hkv, D, P, kv, prefill (ctx_before per request, chunk) or None
+    # lens, Hq, Hkv, D, P, kv, and None, prefill (ctx_before per request,
+    # chunk) or "fused"
     ((1, 33, 200, 700, 2100), 16, 4, 128, 32, "bf16", None),   # matrix-core decode, ranges
     ((5, 64, 65, 900), 8, 8, 128, 64, "bf16", None),           # vector decode (MHA)
     ((1, 129, 1500), 64, 8, 128, 64, "fp8", None),             # fp8 codes from f32 input
     # one pkv_mixed_step call: decode beside chunked prefill on a second stream
     ((5, 300, 1000), 32, 8, 128, 32, "bf16", ((0, 100, 1800), 200)),
+    # one pkv_decode_step call (the append inside the attention launch)
+    ((1, 33, 200, 700, 2100), 16, 4, 128, 32, "bf16", "fused"),
+    ((1, 129, 1500), 64, 8, 128, 64, "fp8", "fused"),
+    ((5, 64, 65, 900), 8, 8, 128, 64, "bf16", "fused"),
 ]
 
 
@@ -48,7 +54,7 @@ def _build(tmp_path) -> str:
     return exe
 
 
-def _write_inputs(d, wl, kp0, vp0):
+def _write_inputs(d, wl, kp0, vp0, fused=False):
     s = wl.spec
     st = wl.step
     kv = B.DTYPE_CODES[s.kv_dtype]
@@ -57,7 +63,11 @@ def _write_inputs(d, wl, kp0, vp0):
             repr(float(wl.sm_scale)), st.num_rows, st.num_tokens, st.block_tables.shape[1],
             B.DTYPE_CODES[s.kv_in_dtype]]
     (d / "meta.txt").write_text(" ".join(str(x) for x in meta) + "\n")
-    files = {"kpool.bin": kp0, "vpool.bin": vp0, "knew.bin": st.k, "vnew.bin": st.v,
+    k_step, v_step = st.k, st.v
+    if fused:
+        (d / "fused.txt").write_text("1\n")
+        k_step, v_step = wk.decode_step_tokens(wl)
+    files = {"kpool.bin": kp0, "vpool.bin": vp0, "knew.bin": k_step, "vnew.bin": v_step,
              "cu.bin": st.cu.astype(np.int32), "start.bin": st.start_pos.astype(np.int32),
              "stepbt.bin": st.block_tables.astype(np.int32), "q.bin": wl.q,
              "bt.bin": wl.block_tables.astype(np.int32),
@@ -82,7 +92,9 @@ def _write_inputs(d, wl, kp0, vp0):
 def test_c_client_append_and_decode_match_oracle(case, tmp_path):
     if shutil.which("gcc") is None:
         pytest.fail("gcc is needed to build the C client")
-    lens, hq, hkv, hd, page, kv, pf = case
+    lens, hq, hkv, hd, page, kv, mode = case
+    fused = mode == "fused"
+    pf = None if fused else mode
     extra = dict(prefill_ctx=pf[0], prefill_chunk=pf[1]) if pf else {}
     spec = wk.custom_spec(lens, num_q_heads=hq, num_kv_heads=hkv, head_dim=hd, page_size=page,
                           q_dtype="bf16", kv_dtype=kv, out_dtype="bf16", **extra)
@@ -94,7 +106,7 @@ def test_c_client_append_and_decode_match_oracle(case, tmp_path):
     exe = _build(tmp_path)
     d = tmp_path / "io"
     d.mkdir()
-    _write_inputs(d, wl, kp0, vp0)
+    _write_inputs(d, wl, kp0, vp0, fused)
     print(f"[c-client] case {case}", flush=True)
     r = subprocess.run([exe, str(d)], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, f"decode_client failed:\n{r.stdout}\n{r.stderr}"

@@ -1,0 +1,148 @@
+"""The fused decode step (pkv_decode_step) on the GPU: each sequence's new
+token is written by the attention launch itself.
+
+Against the oracle: the pools after the step equal the oracle's append of
+the step tokens byte for byte (poison included), and out / lse meet the
+decode bars ("TensorRT-LLM框架解析与高性能推理优化实践" §4.2 and §6.2: the
+block-table write and walk; §6.1: the one-pass softmax).  Against the
+separate calls: pools, out and lse equal pkv_kv_cache_append followed by
+pkv_paged_attn_decode bit for bit, on small cases and on the decode
+workloads at full size."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_cache_277_amd import binding as B
+from paged_kv_cache_277_amd import device as dev
+from paged_kv_cache_277_amd import workloads as wk
+from oracle import attention as oa
+from tests import _support as sup
+from tests.test_gpu_parity import (DECODE_CASES, check_close, check_lse, gpu_cache_from,
+                                   gpu_decode, spec_of)
+
+pytestmark = pytest.mark.gpu
+
+
+def run_step(wl, cache, split=0, k_new=None, v_new=None):
+    s = wl.spec
+    if k_new is None:
+        kn, vn = wk.decode_step_tokens(wl)
+        k_new, v_new = dev._dev(kn, s.kv_in_dtype, "cuda"), dev._dev(vn, s.kv_in_dtype, "cuda")
+    q = dev._dev(wl.q, s.q_dtype, "cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device="cuda")
+    bt = dev._dev(wl.block_tables, "i32", "cuda")
+    lens = dev._dev(wl.context_lens, "i32", "cuda")
+    max_len = int(wl.context_lens.max())
+    ws = B.decode_workspace(cache, wl.num_seqs, s.num_q_heads, max_len, split)
+    B.pkv_decode_step(cache, k_new, v_new, q, out, bt, lens, max_len, float(wl.sm_scale), lse=lse,
+                      split_tokens=split, workspace=ws)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def separate_calls(wl, kp0, vp0, split):
+    cache = gpu_cache_from(wl, kp0, vp0)
+    st, s = wl.step, wl.spec
+    B.pkv_kv_cache_append(cache, dev._dev(st.k, s.kv_in_dtype, "cuda"),
+                          dev._dev(st.v, s.kv_in_dtype, "cuda"), dev._dev(st.cu, "i32", "cuda"),
+                          dev._dev(st.start_pos, "i32", "cuda"),
+                          dev._dev(st.block_tables, "i32", "cuda"))
+    out, lse = gpu_decode(wl, cache, split=split)
+    return cache, out, lse
+
+
+def same_bits(a: torch.Tensor, b: torch.Tensor) -> bool:
+    return torch.equal(a.contiguous().view(torch.uint8), b.contiguous().view(torch.uint8))
+
+
+STEP_CASES = DECODE_CASES + [
+    ((0, 5, 0, 17), 4, 2, 64, 16, "bf16"),                  # empty sequences append nothing
+    ((17, 33, 65, 1), 16, 4, 128, 16, "fp8"),               # new token in a page's first slot
+    ((17, 33, 65, 1), 4, 4, 64, 16, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", STEP_CASES)
+@pytest.mark.parametrize("split", [0, 64])
+def test_decode_step_matches_oracle_and_separate_calls(case, split):
+    spec = spec_of(*case)
+    split = max(split, spec.page_size) if split else 0
+    wl = wk.make_workload(spec, seed=211)
+    kp0, vp0 = sup.oracle_pools(wl, with_step=False)
+    kp1, vp1 = sup.oracle_pools(wl, with_step=True)
+    ref, ref_lse = sup.oracle_decode(wl, kp1, vp1)
+
+    cache = gpu_cache_from(wl, kp0, vp0)
+    print(f"[decode-step] case {case} split {split}", flush=True)
+    out, lse = run_step(wl, cache, split)
+    assert dev.storage_to_numpy(cache.k_pool).tobytes() == kp1.tobytes()
+    assert dev.storage_to_numpy(cache.v_pool).tobytes() == vp1.tobytes()
+    check_close(out, ref, spec)
+    check_lse(lse, ref_lse, spec)
+    if (wl.context_lens == 0).any():
+        z = torch.from_numpy(wl.context_lens == 0).cuda()
+        assert (out[z] == 0).all() and torch.isneginf(lse[z]).all()
+
+    cache2, out2, lse2 = separate_calls(wl, kp0, vp0, split)
+    assert same_bits(out, out2) and same_bits(lse, lse2)
+    assert same_bits(cache.k_pool, cache2.k_pool) and same_bits(cache.v_pool, cache2.v_pool)
+
+
+def test_decode_step_repeated_steps_grow_the_context():
+    """Three steps in a row on one cache, the context of every sequence one
+    token longer each step (positions L-3, L-2, L-1 of the workload's final
+    lengths L; some steps cross into a new page), each checked against the
+    oracle's pools and outputs after the same appends."""
+    spec = spec_of((3, 33, 64, 65, 97, 200), 16, 4, 128, 32, "bf16")
+    wl = wk.make_workload(spec, seed=5)
+    kp, vp = sup.oracle_pools(wl, with_step=False)
+    cache = gpu_cache_from(wl, kp, vp)
+    rng = np.random.default_rng(9)
+    cu = np.arange(wl.num_seqs + 1, dtype=np.int32)
+    for back in (2, 1, 0):
+        lens = (wl.context_lens - back).astype(np.int32)
+        shape = (wl.num_seqs, spec.num_kv_heads, spec.head_dim)
+        kn = wk.bf16_bits_rne(rng.standard_normal(shape).astype(np.float32))
+        vn = wk.bf16_bits_rne(rng.standard_normal(shape).astype(np.float32))
+        oa.kv_cache_append(kp, vp, spec.kv_dtype, kn, vn, spec.kv_in_dtype, cu, lens - 1,
+                           wl.block_tables)
+        wl_t = dataclasses.replace(wl, context_lens=lens)
+        ref, ref_lse = sup.oracle_decode(wl_t, kp, vp)
+        print(f"[decode-step] repeated step, lengths {lens.tolist()}", flush=True)
+        out, lse = run_step(wl_t, cache, 0, dev._dev(kn, "bf16", "cuda"),
+                            dev._dev(vn, "bf16", "cuda"))
+        assert dev.storage_to_numpy(cache.k_pool).tobytes() == kp.tobytes(), back
+        assert dev.storage_to_numpy(cache.v_pool).tobytes() == vp.tobytes(), back
+        check_close(out, ref, spec)
+        check_lse(lse, ref_lse, spec)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("cfg", [1, 2, 4, "4-int8"])
+def test_decode_step_full_size_bits(cfg):
+    """At full size, in the split the benchmark uses: the fused step's pools,
+    out and lse equal the separate append + decode bit for bit.  (The
+    shared-prefix workload is left out: some of its sequences end inside the
+    shared pages, where a step may not write.)"""
+    spec = wk.CONFIGS[cfg] if cfg in wk.CONFIGS else wk.variant(cfg)
+    wl = wk.make_workload(spec)
+    print(f"[decode-step] full size {spec.name}", flush=True)
+    a = dev.upload(wl)
+    a.setup()
+    kn, vn = wk.decode_step_tokens(wl)
+    k_new, v_new = dev._dev(kn, spec.kv_in_dtype, "cuda"), dev._dev(vn, spec.kv_in_dtype, "cuda")
+    kpool0, vpool0 = a.cache.k_pool.clone(), a.cache.v_pool.clone()
+    a.append_step()
+    a.decode()
+    torch.cuda.synchronize()
+    cache2 = B.PagedCache(kpool0, vpool0, a.cache.k_scale, a.cache.v_scale)
+    out2, lse2 = torch.empty_like(a.out), torch.empty_like(a.lse)
+    B.pkv_decode_step(cache2, k_new, v_new, a.q, out2, a.bt, a.lens, a.max_len,
+                      float(wl.sm_scale), lse=lse2, split_tokens=a.split_tokens,
+                      workspace=a.workspace)
+    torch.cuda.synchronize()
+    assert same_bits(a.cache.k_pool, cache2.k_pool) and same_bits(a.cache.v_pool, cache2.v_pool)
+    assert same_bits(a.out, out2) and same_bits(a.lse, lse2)
