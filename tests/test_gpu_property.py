@@ -5,8 +5,9 @@ int8), head size 64 or 128, page size 16..256, 1..4 KV heads with a query
 group of 1..16, decode lengths biased to the edges (0, 1, a page +- 1, two
 pages +- 1) plus random ones, an optional shared prefix, an optional set
 of prefill chunks after random cached lengths, and the context-range sizes
-of the decode and prefill calls, and the launch (separate calls, or one
-mixed-step call with or without a side stream).  One step (append, decode, prefill) runs
+of the decode and prefill calls, and the launch (separate calls, one
+mixed-step call with or without a side stream, or, for decode-only batches,
+one fused decode-step call).  One step (append, decode, prefill) runs
 on the GPU; the pools must equal the oracle's byte for byte and every
 output must meet the format's bar.  (The pages ask for an accuracy check
 after every optimisation step: "4. TensorRT-LLM架构与核心组件…" §4.5.)
@@ -39,12 +40,16 @@ def batches(draw):
     P = draw(st.sampled_from([16, 32, 64, 128, 256]))
     Hkv = draw(st.integers(1, 4))
     G = draw(st.sampled_from([1, 2, 3, 4, 5, 8, 16]))
-    prefix_pages = draw(st.sampled_from([0, 0, 1, 2])) if P <= 64 else 0
+    # the fused decode step takes decode-only batches whose sequences each
+    # append their own token (no prefill, no shared prefix)
+    launch = draw(st.sampled_from(["calls", "mixed_step", "mixed_step_side", "decode_step"]))
+    fused = launch == "decode_step"
+    prefix_pages = draw(st.sampled_from([0, 0, 1, 2])) if P <= 64 and not fused else 0
     edge = st.sampled_from([0, 1, P - 1, P, P + 1, 2 * P - 1, 2 * P + 1])
     lens = draw(st.lists(st.one_of(edge, st.integers(0, 700)), min_size=1, max_size=6))
     if prefix_pages:
         lens = [max(L, 1) for L in lens]        # a prefixed sequence holds at least its token
-    prefill = draw(st.booleans())
+    prefill = False if fused else draw(st.booleans())
     pf_ctx = tuple(draw(st.lists(st.one_of(st.sampled_from([0, 1, P - 1, P]),
                                            st.integers(0, 400)), min_size=1, max_size=3))
                    ) if prefill else ()
@@ -53,7 +58,6 @@ def batches(draw):
     split = draw(st.sampled_from([0, 1, 2, 4])) * max(P, 16)
     # prefill ranges: multiples of 64 (one range for fp32 caches)
     pf_split = 0 if kv == "f32" else draw(st.sampled_from([0, 64, 128, 256]))
-    launch = draw(st.sampled_from(["calls", "mixed_step", "mixed_step_side"]))
     seed = draw(st.integers(0, 2 ** 31 - 1))
     return dict(kv=kv, D=D, P=P, Hkv=Hkv, G=G, prefix_pages=prefix_pages, lens=tuple(lens),
                 pf_ctx=pf_ctx, chunk=chunk, split=split, pf_split=pf_split, launch=launch,
@@ -77,6 +81,8 @@ def test_random_batches_match_oracle(case):
     dw.setup()
     if case["launch"] == "calls":
         dw.step()
+    elif case["launch"] == "decode_step":
+        dw.decode_step()
     else:
         dw.mixed_step(side_stream=torch.cuda.Stream() if case["launch"].endswith("side") else None)
     torch.cuda.synchronize()
