@@ -192,6 +192,26 @@ def test_decode_step_rejects_on_host():
     assert _step(d, k_new=None, v_new=None, B_=0) == B.PKV_OK
 
 
+def test_decode_step_binding_checks_shapes_before_calling():
+    """The Python marshalling of pkv_decode_step rejects mismatched new-token
+    rows before the library is called (host tensors: nothing reaches a
+    device)."""
+    B_, Hkv, G, P, D = 3, 2, 2, 16, 64
+    cache = B.PagedCache(torch.zeros(8, Hkv, P, D, dtype=torch.bfloat16),
+                         torch.zeros(8, Hkv, P, D, dtype=torch.bfloat16))
+    q = torch.zeros(B_, Hkv * G, D, dtype=torch.bfloat16)
+    out = torch.empty_like(q)
+    bt = torch.zeros(B_, 4, dtype=torch.int32)
+    lens = torch.ones(B_, dtype=torch.int32)
+    good = torch.zeros(B_, Hkv, D, dtype=torch.bfloat16)
+    for k_new, v_new in ((torch.zeros(B_ + 1, Hkv, D, dtype=torch.bfloat16), good),
+                         (torch.zeros(B_, Hkv + 1, D, dtype=torch.bfloat16), good),
+                         (good, torch.zeros(B_, Hkv, D + 1, dtype=torch.bfloat16)),
+                         (good.transpose(0, 1).contiguous().transpose(0, 1), good)):
+        with pytest.raises(ValueError):
+            B.DecodeStepCall(cache, k_new, v_new, q, out, bt, lens, 16, 0.125)
+
+
 def test_work_list_rejections():
     """pkv_decode_work_list checks its shape arguments like a decode call
     (no GPU needed: every case fails before anything is launched)."""
