@@ -296,7 +296,10 @@ pkv_status pkv_lse_merge(const pkv_cache_desc* cache, void* out, int32_t out_dty
  * The remaining arguments, the supported dtypes, split_tokens, the
  * workspace and its size are those of pkv_paged_attn_decode.  The page that
  * receives a sequence's new token must not be shared with another sequence
- * of the call.
+ * of the call.  Calls of at least 1024 (sequence, range, KV head) work
+ * items first write a longest-first work list into the workspace (one small
+ * launch, as pkv_decode_work_list); smaller calls are one attention launch
+ * (plus the merge when a sequence spans several ranges).
  * Errors: the checks of pkv_paged_attn_decode; in_dtype other than the
  * append's (PKV_ERR_UNSUPPORTED); k_new or v_new NULL with num_seqs > 0
  * (PKV_ERR_INVALID_ARG).  Nothing is launched on error.

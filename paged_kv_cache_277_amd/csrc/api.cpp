@@ -704,7 +704,17 @@ pkv_status pkv_decode_step(const pkv_cache_desc* cache, const void* k_new, const
     return fail(PKV_ERR_INVALID_ARG, "k_new / v_new must not be NULL");
   a.new_k = k_new;
   a.new_v = v_new;
-  return launch_decode_call(a, static_cast<hipStream_t>(stream));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // A call with enough work items takes them longest first from a work list
+  // (one single-workgroup launch before the attention, as
+  // pkv_decode_work_list); smaller calls stay one attention launch.
+  if (a.ws_acc && pkv::decode_plan_useful(a)) {
+    a.plan = decode_list_area(a);
+    const pkv::DecodeListArgs l{context_lens, a.num_rows, a.split_tokens, a.max_splits, a.plan};
+    if ((st = hip_status(pkv::launch_decode_list(l, s), "decode_step (work list)")) != PKV_OK)
+      return st;
+  }
+  return launch_decode_call(a, s);
 }
 
 pkv_status pkv_paged_attn_chunked_prefill(const pkv_cache_desc* cache, const void* q,

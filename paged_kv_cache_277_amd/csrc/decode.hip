@@ -309,10 +309,16 @@ __global__ __launch_bounds__(256) void decode_partial_vec(AttnArgs a) {
   const int ta = tw0 < t_end ? tw0 : ((t_end - 1) & ~(TOK - 1));
   const int pg0 = btrow[ta >> pshift];
   int pg_next = page_of(1);
+  // The new token lies in the owner wave's last tile: with more than one
+  // tile that one is loaded in the loop, so the store can follow this first
+  // load (whose wait then does not cover it); with one tile it must precede it.
   if constexpr (STEP) {
-    if (step_lane) step_piece.store(a);
+    if (step_lane && nt == 1) step_piece.store(a);
   }
   load(kA, vA, pg0, ta);
+  if constexpr (STEP) {
+    if (step_lane && nt > 1) step_piece.store(a);
+  }
   // step(k): page id of tile k+2, loads of tile k+1 into nxt, score tile k.
   auto step = [&](int k, const u32x4 (&kc)[U], const u32x4 (&vc)[U], u32x4 (&kn)[U],
                   u32x4 (&vn)[U]) {

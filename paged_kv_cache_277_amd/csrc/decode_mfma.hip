@@ -247,10 +247,15 @@ void decode_partial_mfma(AttnArgs a) {
   // Only a range's last tile can hold tokens past its end, so every tile of
   // the main loop is computed without masks.
   TR buf0, buf1;
+  // (Fused step: the new token lies in the owner wave's last tile, loaded
+  // in the loop when the wave has more than one; see decode.hip.)
   if constexpr (STEP) {
-    if (step_lane) step_piece.store(a);
+    if (step_lane && nt == 1) step_piece.store(a);
   }
   load_tile<KVT, D>(buf0, kp, vp, pn0, pn1, ta, t_end, Hkv, j, pshift, loff);
+  if constexpr (STEP) {
+    if (step_lane && nt > 1) step_piece.store(a);
+  }
   pn0 = pq0;                                    // pages of the next tile to load
   pn1 = pq1;
 

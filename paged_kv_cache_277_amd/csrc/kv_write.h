@@ -97,11 +97,12 @@ __device__ __forceinline__ void write_kv_piece(const CacheView& c, const void* k
 // Fused decode step: piece `pc` of the new token's K and V rows of KV head
 // j (position pos of sequence z; input row z of new_k / new_v,
 // [num_seqs][Hkv][D]).  The attention kernels load it early and store it
-// from the lane that later loads that same piece from the pool, just before
-// that lane's first K/V load: the store precedes the load in that thread's
-// program order (no barrier), and the inputs have arrived by then (vector
-// memory waits retire in order, so an earlier store would hold up the page
-// ids' wait until it completed).
+// from the lane that later loads that same piece from the pool, right after
+// that wave's first K/V load (or just before it, when the first tile is the
+// one holding the token): the store precedes the load of the token's row in
+// that thread's program order, so no barrier is needed, and the inputs have
+// arrived by then.  Vector memory waits retire in order, so a store issued
+// before a wait's target loads would hold that wait up until it completed.
 template <int KVT>
 struct StepPiece {
   KvInput<KVT> in;
