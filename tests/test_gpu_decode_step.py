@@ -146,3 +146,43 @@ def test_decode_step_full_size_bits(cfg):
     torch.cuda.synchronize()
     assert same_bits(a.cache.k_pool, cache2.k_pool) and same_bits(a.cache.v_pool, cache2.v_pool)
     assert same_bits(a.out, out2) and same_bits(a.lse, lse2)
+
+
+@pytest.mark.parametrize("case", [((7, 33, 64, 100), 4, 4, 64, 16, "f32"),
+                                  ((40, 300, 1000, 2100), 32, 8, 128, 32, "bf16")])
+def test_decode_step_graph_replays_match_eager(case):
+    """One pkv_decode_step captured as a HIP graph and replayed three times,
+    with eager steps in between, reproduces the eager step bit for bit (the
+    step rewrites the same token each time, so the pools do not change)."""
+    spec = spec_of(*case)
+    wl = wk.make_workload(spec, seed=8)
+    dw = dev.upload(wl)
+    dw.setup()
+    dw.decode_step()
+    torch.cuda.synchronize()
+    ref_out, ref_lse = dw.out.clone(), dw.lse.clone()
+    ref_k, ref_v = dw.cache.k_pool.clone(), dw.cache.v_pool.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):                     # warm the capture stream once
+        dw.decode_step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dw.decode_step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        dw.out.zero_()
+        dw.lse.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert same_bits(dw.out, ref_out) and same_bits(dw.lse, ref_lse), f"replay {rep}"
+        assert same_bits(dw.cache.k_pool, ref_k) and same_bits(dw.cache.v_pool, ref_v)
+        dw.decode_step()                           # eager work between replays
+        torch.cuda.synchronize()
+        assert same_bits(dw.out, ref_out)
+    kp, vp = sup.oracle_pools(wl)
+    ref, _ = sup.oracle_decode(wl, kp, vp)
+    check_close(dw.out, ref, spec)
