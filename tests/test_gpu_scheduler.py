@@ -1,6 +1,7 @@
 """Scheduler-driven steps on the GPU: the host scheduler's plans (block
 tables, positions, prefill chunks and decode tokens, evictions and
-recomputation) drive pkv_mixed_step, and every step's outputs are checked
+recomputation) drive pkv_mixed_step, or, on every other step that has only
+decode items, the fused pkv_decode_step; every step's outputs are checked
 against the oracle over the same pages."""
 import numpy as np
 import pytest
@@ -78,6 +79,7 @@ def test_scheduler_driven_steps_match_oracle(policy, with_prefix):
             k[:plen], v[:plen] = prefix_data[pid]
         reqs[rid] = (q, k, v)
     steps = 0
+    fused_steps = 0
     prefixed_attended = 0
     evicted = []
     while sched.stats()["waiting"] + sched.stats()["running"] > 0:
@@ -122,7 +124,16 @@ def test_scheduler_driven_steps_match_oracle(policy, with_prefix):
             pre = B.prefill_batch(pq, pout, pcu, pctx, pbt, a.max_chunk, a.max_total, lse=plse,
                                   split_tokens=64, workspace=ws2)
             keep += [pq, pbt, pcu, pctx, ws2]
-        B.pkv_mixed_step(cache, app, dec, pre, scale, side_stream=side)
+        if pre is None and dec is not None and steps % 2 == 0:
+            # decode-only step: each item's one new token (position L - 1)
+            # written by the attention launch itself
+            fk = _bf16(np.stack([reqs[items[i][0]][1][items[i][3]] for i in a.dec_idx]))
+            fv = _bf16(np.stack([reqs[items[i][0]][2][items[i][3]] for i in a.dec_idx]))
+            B.pkv_decode_step(cache, fk, fv, dq, dout, dbt, dl, dmax, scale, lse=dlse,
+                              split_tokens=32, workspace=ws)
+            fused_steps += 1
+        else:
+            B.pkv_mixed_step(cache, app, dec, pre, scale, side_stream=side)
         torch.cuda.synchronize()
         # the oracle: same appends into host pages, then attention over them
         oa.kv_cache_append(kp, vp, "bf16", k_new, v_new, "bf16", a.app_cu, a.app_start,
@@ -143,8 +154,10 @@ def test_scheduler_driven_steps_match_oracle(policy, with_prefix):
     assert np.array_equal(kd.view(torch.int16).cpu().numpy().view(np.uint16), kp)
     assert np.array_equal(vd.view(torch.int16).cpu().numpy().view(np.uint16), vp)
     st = sched.stats()
-    print(f"[scheduler] policy {policy} prefix {with_prefix}: {steps} steps, "
-          f"{st['preemptions']} preemptions, {prefixed_attended} prefixed items", flush=True)
+    print(f"[scheduler] policy {policy} prefix {with_prefix}: {steps} steps "
+          f"({fused_steps} fused decode steps), {st['preemptions']} preemptions, "
+          f"{prefixed_attended} prefixed items", flush=True)
+    assert fused_steps > 0
     if policy == B.PKV_SCHED_AGGRESSIVE:
         assert st["preemptions"] > 0, "the trace should force evictions"
     else:
