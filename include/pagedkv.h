@@ -331,7 +331,9 @@ pkv_status pkv_decode_step(const pkv_cache_desc* cache,
  * start at zero; it keeps the last call's contents.  Every call on one GPU
  * shares that GPU's array: calls that overlap in time on one GPU (on
  * different streams, or from several threads without ordering) race and give
- * wrong results; calls on one stream are ordered and safe.
+ * wrong results; calls on one stream are ordered and safe.  The array used
+ * is the current device's, so `stream` must belong to the current device;
+ * a stream of another device returns PKV_ERR_INVALID_ARG.
  * ------------------------------------------------------------------------ */
 #define PKV_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
 pkv_status pkv_paged_attn_decode_noalloc(const pkv_cache_desc* cache,

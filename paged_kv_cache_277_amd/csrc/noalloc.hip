@@ -28,9 +28,10 @@ constexpr int kMaxDevices = 64;
 std::mutex g_mu;
 void* g_ptr[kMaxDevices];          // device address of `scratch`, per device
 
-// The device address of this device's array (looked up on the first call on
-// the device).
-pkv_status scratch_on_current_device(void** out) {
+// The device address of the current device's array (looked up on the first
+// call on the device).  The kernels run on `stream`'s device, so that must be
+// the current device: the array of another device is not this one.
+pkv_status scratch_on_current_device(hipStream_t stream, void** out) {
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) {
@@ -40,6 +41,18 @@ pkv_status scratch_on_current_device(void** out) {
   if (dev < 0 || dev >= kMaxDevices) {
     pkv_detail::set_error("decode_noalloc: device index out of range");
     return PKV_ERR_UNSUPPORTED;
+  }
+  hipDevice_t sdev = -1;
+  e = hipStreamGetDevice(stream, &sdev);
+  if (e != hipSuccess) {
+    pkv_detail::set_error(std::string("decode_noalloc: stream's device: ") + hipGetErrorString(e));
+    return PKV_ERR_HIP;
+  }
+  if (sdev != dev) {
+    pkv_detail::set_error("decode_noalloc: the stream belongs to device " + std::to_string(sdev) +
+                          " but device " + std::to_string(dev) +
+                          " is current; make the stream's device current first");
+    return PKV_ERR_INVALID_ARG;
   }
   std::lock_guard<std::mutex> lock(g_mu);
   if (!g_ptr[dev]) {
@@ -80,7 +93,7 @@ pkv_status pkv_paged_attn_decode_noalloc(const pkv_cache_desc* cache, const void
     return PKV_ERR_INVALID_ARG;
   }
   void* ws = nullptr;
-  pkv_status st = scratch_on_current_device(&ws);
+  pkv_status st = scratch_on_current_device(static_cast<hipStream_t>(stream), &ws);
   if (st != PKV_OK) return st;
   return pkv_paged_attn_decode(cache, q, q_dtype, out, out_dtype, lse, block_tables, bt_stride,
                                context_lens, num_seqs, num_q_heads, max_context_len, sm_scale,
