@@ -169,8 +169,23 @@ def version() -> str:
 
 
 # ------------------------------------------------------------ helpers -------
+_gpu_present: Optional[bool] = None
+
+
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
-    return None if t is None else t.data_ptr()
+    """Device address of a tensor the library reads or writes.  Where a GPU
+    is present, a tensor in host memory is refused here: its address would
+    reach a kernel, which cannot read it.  (Empty tensors are never read.)"""
+    global _gpu_present
+    if t is None:
+        return None
+    if t.device.type != "cuda" and t.numel() > 0:
+        if _gpu_present is None:
+            _gpu_present = torch.cuda.is_available()
+        if _gpu_present:
+            raise ValueError(f"a tensor on {t.device} was passed where the library takes GPU "
+                             "memory")
+    return t.data_ptr()
 
 
 def _stream(stream) -> Optional[int]:

@@ -212,6 +212,35 @@ def test_decode_step_binding_checks_shapes_before_calling():
             B.DecodeStepCall(cache, k_new, v_new, q, out, bt, lens, 16, 0.125)
 
 
+def test_binding_refuses_host_tensors_where_a_gpu_is_present(monkeypatch):
+    """Where a GPU is present, the marshalling refuses a tensor in host memory
+    before the library is called (its address would reach a kernel); empty
+    tensors, never read, pass.  Without a GPU, host tensors go on to the
+    library's own host-side checks (the other tests here)."""
+    B_, Hkv, P, D = 2, 2, 16, 64
+    cache = B.PagedCache(torch.zeros(8, Hkv, P, D, dtype=torch.bfloat16),
+                         torch.zeros(8, Hkv, P, D, dtype=torch.bfloat16))
+    q = torch.zeros(B_, Hkv, D, dtype=torch.bfloat16)
+    out = torch.empty_like(q)
+    bt = torch.zeros(B_, 4, dtype=torch.int32)
+    lens = torch.ones(B_, dtype=torch.int32)
+
+    class NoCall:
+        def __getattr__(self, name):
+            def call(*args):
+                raise AssertionError(f"{name} was called")
+            return call
+
+    monkeypatch.setattr(B, "lib", lambda: NoCall())
+    monkeypatch.setattr(B, "_gpu_present", True)
+    with pytest.raises(ValueError, match="GPU memory"):
+        B.pkv_paged_attn_decode(cache, q, out, bt, lens, 16, 0.125)
+    with pytest.raises(ValueError, match="GPU memory"):
+        B.PagedCache(torch.zeros(8, Hkv, P, D, dtype=torch.bfloat16),
+                     torch.zeros(8, Hkv, P, D, dtype=torch.bfloat16))
+    assert B._ptr(torch.zeros(0, dtype=torch.int32)) is not None
+
+
 def test_work_list_rejections():
     """pkv_decode_work_list checks its shape arguments like a decode call
     (no GPU needed: every case fails before anything is launched)."""
