@@ -9,7 +9,8 @@
 //
 // Launch: one workgroup per new token; its threads cover the token's
 // Hkv x head_dim row in 16-byte output pieces, so every page row is written
-// with full 16-byte stores and the packed input is read contiguously.
+// with full 16-byte stores and the packed input is read contiguously.  The
+// workgroup size is a multiple of 64 (the row lookup is wave-wide).
 #include "decode_list.h"
 #include "kv_write.h"
 #include "pkv_device.h"
@@ -26,15 +27,23 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     return;
   }
   const int t = blockIdx.x;
+  const int D = a.c.head_dim, Hkv = a.c.num_kv_heads;
+  const int pieces = D / EPL;                    // per head
+  const int total = Hkv * pieces;
+  // The input does not depend on where the token goes: the first piece's
+  // loads are issued before the lookups of its row, position and page.
+  const int c0 = threadIdx.x, j0 = c0 / pieces, pc0 = c0 % pieces;
+  KvInput<KVT> in0;
+  if (c0 < total)
+    in0 = load_kv_input<KVT>(a.c, a.k_new, a.v_new, ((size_t)t * Hkv + j0) * D + (size_t)pc0 * EPL,
+                             j0);
   const int r = owner_row(a.cu, a.num_rows, t);
   const int pos = a.start_pos[r] + (t - a.cu[r]);
   const int P = a.c.page_size;
   const int page = a.bt[(size_t)r * a.bt_stride + pos / P];
   const int slot = pos % P;
-  const int D = a.c.head_dim, Hkv = a.c.num_kv_heads;
-  const int pieces = D / EPL;                    // per head
-  const int total = Hkv * pieces;
-  for (int c = threadIdx.x; c < total; c += blockDim.x) {
+  if (c0 < total) store_kv_input<KVT>(a.c, in0, kv_piece_offset<KVT>(a.c, page, j0, slot, pc0));
+  for (int c = c0 + blockDim.x; c < total; c += blockDim.x) {
     const int j = c / pieces, pc = c % pieces;
     const size_t src_e = ((size_t)t * Hkv + j) * D + (size_t)pc * EPL;   // input element
     write_kv_piece<KVT>(a.c, a.k_new, a.v_new, src_e, kv_piece_offset<KVT>(a.c, page, j, slot, pc), j);
