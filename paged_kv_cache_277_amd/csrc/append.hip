@@ -19,6 +19,22 @@
 namespace pkv {
 namespace {
 
+// Request owning packed token t: the largest r < n with cu[r] <= t
+// (cu[0] = 0, non-decreasing, n >= 1, t < cu[n]), which is the number of
+// rows 1 .. n-1 that start at or before t.  The wave's lanes test 64 offsets
+// per load and a ballot counts them, so the lookup costs one load latency per
+// 64 rows instead of one per step of a binary search.  Every lane of the
+// wave must be active; the result is wave-uniform.
+__device__ __forceinline__ int owner_row(const int32_t* cu, int n, int t) {
+  const int lane = threadIdx.x & 63;
+  int r = 0;
+  for (int base = 1; base < n; base += 64) {
+    const int i = base + lane;
+    r += __popcll(__ballot(i < n && cu[i] <= t));
+  }
+  return r;
+}
+
 template <int KVT>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   constexpr int EPL = 16 / KvBytes<KVT>::value;  // cache elements per 16-byte piece
