@@ -11,7 +11,7 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
-    config.addinivalue_line("markers", "slow: full-size workloads (GPU box)")
+    config.addinivalue_line("markers", "slow: full-size workloads (need a GPU)")
 
 
 def pytest_collection_modifyitems(config, items):
