@@ -451,8 +451,9 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: the decode path shards by sequence or KV head "
-              "with no exchange, and this build runs on a single MI355X (use --gpus 1).",
+        print("bench.py measures one GPU only (use --gpus 1): the decode path would shard by "
+              "sequence or KV head with no exchange, so the throughput of N GPUs is N times "
+              "that of one GPU's share.",
               file=sys.stderr)
         return 2
 

@@ -69,8 +69,8 @@ def _status(fn):
 
 
 class RecordingScheduler:
-    """B.Scheduler that records every call and its answer in the driver's
-    command format."""
+    """B.Scheduler that records every call and its answer in the command
+    format of the sanitized C program that replays them."""
 
     def __init__(self, inner, cfg, log):
         self.inner, self.log = inner, log
